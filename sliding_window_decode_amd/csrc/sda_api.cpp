@@ -1,0 +1,387 @@
+// sda_api.cpp -- host side of the C ABI declared in include/sda.h: argument checks, the plan, the
+// workspace layout and the kernel launches. Nothing here allocates device memory or synchronizes.
+//
+// The checks follow the validation block of FlashMLA sparse_decode.h (sparse_attn_decode_interface):
+// MQA only (one latent row per slot), d_qk in {576, 512} with d_v = 512, a positive list width,
+// the extra cache and extra indices given together, and record sizes that match the format.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return SDA_ERR_HIP;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+  int s = 0;
+  while ((int64_t(1) << s) < v) ++s;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool supported_heads(int H) { return H == 16 || H == 32 || H == 64 || H == 128; }
+
+int check_cache(const sda_cache* c, int d_qk, const char* which) {
+  static char msg[256];
+  if (!c || !c->base) {
+    snprintf(msg, sizeof(msg), "%s cache: NULL", which);
+    return fail(SDA_ERR_INVALID_ARG, msg);
+  }
+  const int rec = sda_record_bytes(c->format);
+  if (rec < 0) {
+    snprintf(msg, sizeof(msg), "%s cache: unknown format %d", which, c->format);
+    return fail(SDA_ERR_UNSUPPORTED, msg);
+  }
+  if (sda_format_dims(c->format) != d_qk) {
+    snprintf(msg, sizeof(msg), "%s cache: format %d holds %d dims, d_qk is %d", which, c->format,
+             sda_format_dims(c->format), d_qk);
+    return fail(SDA_ERR_UNSUPPORTED, msg);
+  }
+  if (!aligned(c->base, 16)) return fail(SDA_ERR_INVALID_ARG, "cache base must be 16-byte aligned");
+  if (c->num_pages < 1 || !is_pow2(c->page_size))
+    return fail(SDA_ERR_INVALID_ARG, "cache needs num_pages >= 1 and a power-of-two page_size");
+  if (c->num_pages * (int64_t)c->page_size >= (int64_t(1) << 31))
+    return fail(SDA_ERR_INVALID_ARG, "cache holds 2^31 slots or more");
+  if (c->page_stride < (int64_t)c->page_size * rec || (c->page_stride % 16) != 0)
+    return fail(SDA_ERR_INVALID_ARG, "page_stride must be >= page_size * record bytes and a multiple of 16");
+  if ((c->format == SDA_FP8_SLOTSCALE) != (c->slot_scale != nullptr))
+    return fail(SDA_ERR_INVALID_ARG, "slot_scale is required for SDA_FP8_SLOTSCALE and only for it");
+  return SDA_OK;
+}
+
+int check_list(const sda_list* l, const char* which) {
+  static char msg[256];
+  if (!l || !l->idx) {
+    snprintf(msg, sizeof(msg), "%s list: NULL", which);
+    return fail(SDA_ERR_INVALID_ARG, msg);
+  }
+  if (l->width < 1 || l->row_stride < l->width) {
+    snprintf(msg, sizeof(msg), "%s list: width must be >= 1 and row_stride >= width", which);
+    return fail(SDA_ERR_INVALID_ARG, msg);
+  }
+  return SDA_OK;
+}
+
+int check_plan(const sda_plan* plan, int H) {
+  if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->num_parts < 1 || plan->num_parts > (1 << 20)) return fail(SDA_ERR_INVALID_ARG, "plan.num_parts out of range");
+  const int hb = plan->heads_per_group;
+  if (!(hb == 16 || hb == 32) || H % hb != 0)
+    return fail(SDA_ERR_UNSUPPORTED, "plan.heads_per_group must be 16 or 32 and divide H");
+  if (plan->fixed_overhead < 0 || plan->fixed_overhead > 1024)
+    return fail(SDA_ERR_INVALID_ARG, "plan.fixed_overhead out of range");
+  if (plan->precision != 1 && plan->precision != 3) return fail(SDA_ERR_INVALID_ARG, "plan.precision must be 1 or 3");
+  return SDA_OK;
+}
+
+struct WorkspaceLayout {
+  size_t o_acc, lse_acc, meta, num_splits, total;
+};
+
+WorkspaceLayout layout_of(int T, int H, int d_v, int P) {
+  WorkspaceLayout w;
+  const size_t splits = (size_t)T + (size_t)P;
+  w.o_acc = 0;
+  w.lse_acc = round_up(w.o_acc + splits * H * d_v * sizeof(float), 256);
+  w.meta = round_up(w.lse_acc + splits * H * sizeof(float), 256);
+  w.num_splits = round_up(w.meta + (size_t)P * SDA_META_INTS * sizeof(int32_t), 256);
+  w.total = round_up(w.num_splits + ((size_t)T + 1) * sizeof(int32_t), 256);
+  return w;
+}
+
+sda::ListDev list_dev(const sda_cache* c, const sda_list* l) {
+  sda::ListDev d;
+  memset(&d, 0, sizeof(d));
+  d.idx = l->idx;
+  d.lens = l->lens;
+  d.base = (const uint8_t*)c->base;
+  d.slot_scale = c->slot_scale;
+  d.row_stride = l->row_stride;
+  d.page_stride = c->page_stride;
+  d.width = l->width;
+  d.slots = (int32_t)(c->num_pages * c->page_size);
+  d.page_shift = ilog2(c->page_size);
+  d.format = c->format;
+  d.rec = sda_record_bytes(c->format);
+  return d;
+}
+
+sda::SchedParams sched_params(int T, const sda_list* list, const sda_list* extra, const sda_plan* plan, int32_t* meta,
+                              int32_t* num_splits) {
+  sda::SchedParams s;
+  memset(&s, 0, sizeof(s));
+  s.lens[0] = list->lens;
+  s.width[0] = list->width;
+  s.nlists = 1;
+  if (extra) {
+    s.lens[1] = extra->lens;
+    s.width[1] = extra->width;
+    s.nlists = 2;
+  }
+  s.T = T;
+  s.num_parts = plan->num_parts;
+  s.F = plan->fixed_overhead;
+  s.meta = meta;
+  s.num_splits = num_splits;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sda_status_string(int status) {
+  switch (status) {
+    case SDA_OK: return "ok";
+    case SDA_ERR_INVALID_ARG: return "invalid argument";
+    case SDA_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case SDA_ERR_WORKSPACE: return "workspace too small";
+    case SDA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sda_last_error(void) { return g_last_error; }
+
+int sda_record_bytes(int format) {
+  switch (format) {
+    case SDA_FP8_SLOTSCALE: return 512;
+    case SDA_FP8_528: return 528;
+    case SDA_NVFP4_288: return 288;
+    case SDA_V32_656: return 656;
+    default: return -1;
+  }
+}
+
+int sda_format_dims(int format) {
+  switch (format) {
+    case SDA_FP8_SLOTSCALE:
+    case SDA_FP8_528:
+    case SDA_NVFP4_288: return 512;
+    case SDA_V32_656: return 576;
+    default: return -1;
+  }
+}
+
+int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cus, sda_plan* plan) {
+  if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
+  if (T < 1 || width < 1 || extra_width < 0) return fail(SDA_ERR_INVALID_ARG, "T and width must be >= 1");
+  if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
+  if (d_qk != 512 && d_qk != 576) return fail(SDA_ERR_UNSUPPORTED, "d_qk must be 512 or 576");
+  if (num_cus <= 0) num_cus = 256;
+  // Heads per workgroup: the largest group that still gives every CU a workgroup by tokens x head
+  // groups alone; smaller groups re-read the token's rows (from L2) but need no split partials.
+  int hb = H < 32 ? H : 32;
+  while (hb > 16 && (int64_t)T * (H / hb) < num_cus) hb /= 2;
+  const int groups = H / hb;
+  int parts = (2 * num_cus) / groups;
+  if (parts < 1) parts = 1;
+  plan->num_parts = parts;
+  plan->heads_per_group = hb;
+  plan->fixed_overhead = 2;
+  plan->precision = 3;
+  return SDA_OK;
+}
+
+size_t sda_workspace_bytes(int T, int H, int d_v, const sda_plan* plan) {
+  if (!plan || T < 1 || H < 1 || d_v < 1 || plan->num_parts < 1) return 0;
+  return layout_of(T, H, d_v, plan->num_parts).total;
+}
+
+int sda_get_sched_meta(int T, const sda_list* list, const sda_list* extra, const sda_plan* plan, int32_t* meta,
+                       int32_t* num_splits, void* stream) {
+  if (T < 1) return fail(SDA_ERR_INVALID_ARG, "T must be >= 1");
+  int rc = check_list(list, "main");
+  if (rc) return rc;
+  if (extra && (rc = check_list(extra, "extra"))) return rc;
+  if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
+  if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
+  hipError_t e = sda::launch_sched(sched_params(T, list, extra, plan, meta, num_splits), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
+  return SDA_OK;
+}
+
+int sda_get_sched_meta_host(int T, const int32_t* lens, int width, const int32_t* extra_lens, int extra_width,
+                            const sda_plan* plan, int32_t* meta, int32_t* num_splits) {
+  if (T < 1 || width < 1 || extra_width < 0) return fail(SDA_ERR_INVALID_ARG, "T and width must be >= 1");
+  if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
+  if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
+  const int P = plan->num_parts, F = plan->fixed_overhead;
+  int64_t total = 0;
+  for (int t = 0; t < T; ++t) {
+    const int n0 = sda::clamp_len(lens, width, t);
+    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, extra_width, t) : 0;
+    total += sda::token_tiles(n0, n1) + F;
+  }
+  const int64_t Q = sda::part_quantum(total, P);
+  int64_t cum = 0;
+  int32_t splits = 0;
+  for (int t = 0; t < T; ++t) {
+    const int n0 = sda::clamp_len(lens, width, t);
+    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, extra_width, t) : 0;
+    const int nt = sda::token_tiles(n0, n1);
+    const int64_t pos0 = cum + F;
+    const int64_t p0 = pos0 / Q, p1 = (pos0 + nt - 1) / Q;
+    num_splits[t] = splits;
+    splits += (int32_t)(p1 - p0 + 1);
+    const int64_t prev_last = (cum == 0) ? -1 : (cum - 1) / Q;
+    for (int64_t pp = prev_last + 1; pp <= p1; ++pp) {
+      const int64_t bi = pp * Q - pos0 > 0 ? pp * Q - pos0 : 0;
+      int32_t* m = meta + pp * SDA_META_INTS;
+      m[0] = t;
+      m[1] = (int32_t)bi;
+      m[4] = pp >= p0 ? (int32_t)(pp - p0) : 0;
+      m[5] = m[6] = m[7] = 0;
+      if (pp > 0) {
+        meta[(pp - 1) * SDA_META_INTS + 2] = t;
+        meta[(pp - 1) * SDA_META_INTS + 3] = (int32_t)bi;
+      }
+    }
+    cum += nt + F;
+  }
+  num_splits[T] = splits;
+  const int64_t last = (total - 1) / Q;
+  for (int64_t pp = last + 1; pp < P; ++pp) {
+    int32_t* m = meta + pp * SDA_META_INTS;
+    m[0] = T; m[1] = 0; m[2] = T; m[3] = 0; m[4] = 0; m[5] = 0; m[6] = 0; m[7] = 0;
+  }
+  meta[last * SDA_META_INTS + 2] = T;
+  meta[last * SDA_META_INTS + 3] = 0;
+  return SDA_OK;
+}
+
+int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                           const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                           const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                           const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                           void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                           void* stream) {
+  if (!q || !out || !lse) return fail(SDA_ERR_INVALID_ARG, "q, out and lse are required");
+  if (T < 1) return fail(SDA_ERR_INVALID_ARG, "T must be >= 1");
+  if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
+  if (!((d_qk == 512 || d_qk == 576) && d_v == 512))
+    return fail(SDA_ERR_UNSUPPORTED, "(d_qk, d_v) must be (512, 512) or (576, 512)");
+  if (!aligned(q, 16) || q_stride_h % 8 || q_stride_t % 8 || q_stride_h < d_qk || q_stride_t < 0)
+    return fail(SDA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (!aligned(out, 16) || out_stride_h % 8 || out_stride_t % 8 || out_stride_h < d_v || out_stride_t < 0)
+    return fail(SDA_ERR_INVALID_ARG, "out must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
+  int rc;
+  if ((rc = check_cache(cache, d_qk, "main"))) return rc;
+  if ((rc = check_list(list, "main"))) return rc;
+  if ((extra_cache == nullptr) != (extra_list == nullptr))
+    return fail(SDA_ERR_INVALID_ARG, "extra_cache and extra_list must be given together");
+  if (extra_cache) {
+    if ((rc = check_cache(extra_cache, d_qk, "extra"))) return rc;
+    if ((rc = check_list(extra_list, "extra"))) return rc;
+  }
+  if ((rc = check_plan(plan, H))) return rc;
+  if ((meta == nullptr) != (num_splits == nullptr))
+    return fail(SDA_ERR_INVALID_ARG, "meta and num_splits must be given together");
+  const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
+  if (!workspace || !aligned(workspace, 256)) return fail(SDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < wl.total) return fail(SDA_ERR_WORKSPACE, "workspace smaller than sda_workspace_bytes()");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (!meta) {
+    int32_t* m = (int32_t*)(ws + wl.meta);
+    int32_t* ns = (int32_t*)(ws + wl.num_splits);
+    hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
+    if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
+    meta = m;
+    num_splits = ns;
+  }
+
+  sda::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)q;
+  p.q_st = q_stride_t;
+  p.q_sh = q_stride_h;
+  p.out = (uint16_t*)out;
+  p.o_st = out_stride_t;
+  p.o_sh = out_stride_h;
+  p.lse = lse;
+  p.l_st = lse_stride_t;
+  p.sink = attn_sink;
+  p.meta = meta;
+  p.num_splits = num_splits;
+  p.o_acc = (float*)(ws + wl.o_acc);
+  p.lse_acc = (float*)(ws + wl.lse_acc);
+  p.lst[0] = list_dev(cache, list);
+  p.nlists = 1;
+  if (extra_cache) {
+    p.lst[1] = list_dev(extra_cache, extra_list);
+    p.nlists = 2;
+  }
+  p.T = T;
+  p.H = H;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision, st);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+
+  sda::CombineParams c;
+  memset(&c, 0, sizeof(c));
+  c.o_acc = p.o_acc;
+  c.lse_acc = p.lse_acc;
+  c.num_splits = num_splits;
+  c.sink = attn_sink;
+  c.out = (uint16_t*)out;
+  c.o_st = out_stride_t;
+  c.o_sh = out_stride_h;
+  c.lse = lse;
+  c.l_st = lse_stride_t;
+  c.T = T;
+  c.H = H;
+  e = sda::launch_combine(c, st);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return SDA_OK;
+}
+
+int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float* lse_accum, const int32_t* num_splits,
+                       const float* attn_sink, void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                       int64_t lse_stride_t, void* stream) {
+  if (T < 1 || H < 1) return fail(SDA_ERR_INVALID_ARG, "T and H must be >= 1");
+  if (d_v != 512) return fail(SDA_ERR_UNSUPPORTED, "d_v must be 512");
+  if (!o_accum || !lse_accum || !num_splits || !out || !lse) return fail(SDA_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(o_accum, 16) || !aligned(out, 8) || out_stride_h % 4 || out_stride_t % 4 || out_stride_h < d_v)
+    return fail(SDA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, out 8-byte aligned with strides in 4s");
+  if (lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
+  sda::CombineParams c;
+  memset(&c, 0, sizeof(c));
+  c.o_acc = o_accum;
+  c.lse_acc = lse_accum;
+  c.num_splits = num_splits;
+  c.sink = attn_sink;
+  c.out = (uint16_t*)out;
+  c.o_st = out_stride_t;
+  c.o_sh = out_stride_h;
+  c.lse = lse;
+  c.l_st = lse_stride_t;
+  c.T = T;
+  c.H = H;
+  hipError_t e = sda::launch_combine(c, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return SDA_OK;
+}
+
+}  // extern "C"

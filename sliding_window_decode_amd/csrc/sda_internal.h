@@ -1,0 +1,101 @@
+// sda_internal.h -- declarations shared by the host API (sda_api.cpp) and the HIP kernels
+// (sda_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sda.h"
+
+namespace sda {
+
+constexpr int kTileRows = 64;     // list positions per scheduler tile
+constexpr int kDv = 512;          // value dims (the first 512 dims of the latent row)
+
+// One slot list with its cache, in the form the kernels read it.
+struct ListDev {
+  const int32_t* idx;
+  const int32_t* lens;       // nullptr = width
+  const uint8_t* base;
+  const float* slot_scale;   // FP8_SLOTSCALE only
+  int64_t row_stride;
+  int64_t page_stride;
+  int32_t width;
+  int32_t slots;             // num_pages * page_size (< 2^31)
+  int32_t page_shift;
+  int32_t format;
+  int32_t rec;               // record bytes
+  int32_t pad_;
+};
+
+struct DecodeParams {
+  const uint16_t* q;         // bf16 bits
+  int64_t q_st, q_sh;        // element strides
+  uint16_t* out;             // bf16 bits
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t l_st;
+  const float* sink;         // [H] or nullptr
+  const int32_t* meta;
+  const int32_t* num_splits;
+  float* o_acc;              // [splits][H][512]
+  float* lse_acc;            // [splits][H]
+  ListDev lst[2];
+  int nlists;
+  int T, H;
+  float scale_log2;          // softmax scale * log2(e)
+};
+
+struct SchedParams {
+  const int32_t* lens[2];    // nullptr = width
+  int32_t width[2];
+  int nlists;
+  int T;
+  int num_parts;
+  int F;                     // fixed overhead per token, in tiles
+  int32_t* meta;
+  int32_t* num_splits;
+};
+
+struct CombineParams {
+  const float* o_acc;
+  const float* lse_acc;
+  const int32_t* num_splits;
+  const float* sink;
+  uint16_t* out;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t l_st;
+  int T, H;
+};
+
+// ---------------------------------------------------------------- scheduling math (host + device)
+//
+// Token t has tiles(t) = max(1, ceil(n_main/64) + ceil(n_extra/64)) tiles, n = clamp(len, 0, width),
+// and costs tiles(t) + F. On the cumulative cost axis token t starts at cum(t); its tile i sits at
+// cum(t) + F + i and belongs to part floor(position / Q) with Q = ceil(total / num_parts). Parts are
+// therefore contiguous ranges of the (token, tile) sequence, in order.
+
+__host__ __device__ inline int clamp_len(const int32_t* lens, int width, int t) {
+  int n = lens ? lens[t] : width;
+  return n < 0 ? 0 : (n > width ? width : n);
+}
+
+__host__ __device__ inline int token_tiles(int n0, int n1) {
+  int tl = (n0 + kTileRows - 1) / kTileRows + (n1 + kTileRows - 1) / kTileRows;
+  return tl < 1 ? 1 : tl;
+}
+
+__host__ __device__ inline int64_t part_quantum(int64_t total, int num_parts) {
+  int64_t q = (total + num_parts - 1) / num_parts;
+  return q < 1 ? 1 : q;
+}
+
+// ---------------------------------------------------------------- launchers (sda_kernels.hip)
+
+hipError_t launch_sched(const SchedParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
+                         hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace sda

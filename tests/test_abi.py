@@ -1,0 +1,227 @@
+"""The C ABI without a GPU: the library loads, exports what include/sda.h declares, rejects bad
+arguments before touching the device, and its host scheduler partitions the work correctly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sliding_window_decode_amd as sda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "sda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sda_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 10
+    L = sda.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sda.EXPORTED_SYMBOLS)
+
+
+def test_status_strings():
+    L = sda.lib()
+    for st in (0, -1, -2, -3, -4):
+        assert L.sda_status_string(st)
+    assert L.sda_status_string(99) == b"unknown status"
+
+
+def test_format_tables_match_generators():
+    import workloads as wl
+    L = sda.lib()
+    for f, b in wl.RECORD_BYTES.items():
+        assert L.sda_record_bytes(f) == b
+        assert L.sda_format_dims(f) == wl.D_QK[f]
+    assert L.sda_record_bytes(7) == -1
+
+
+@pytest.mark.parametrize("T,H,dqk,W,X", [(4, 16, 512, 128, 0), (64, 128, 512, 128, 0), (256, 32, 512, 128, 512),
+                                         (512, 16, 512, 128, 2048), (128, 128, 576, 2048, 0)])
+def test_make_plan_and_workspace(T, H, dqk, W, X):
+    plan = sda.make_plan(T, H, dqk, W, X)
+    assert plan.num_parts >= 1 and H % plan.heads_per_group == 0 and plan.precision == 3
+    ws = sda.workspace_bytes(T, H, 512, plan)
+    assert ws >= (T + plan.num_parts) * H * 512 * 4 and ws % 256 == 0
+
+
+def test_make_plan_rejects_unsupported():
+    for args in [(4, 24, 512, 128, 0), (4, 16, 640, 128, 0), (0, 16, 512, 128, 0), (4, 16, 512, 0, 0)]:
+        with pytest.raises(sda.SdaError):
+            sda.make_plan(*args)
+
+
+class _FakeTensor:
+    """A stand-in exposing data_ptr/stride/shape; its address is never dereferenced because every call
+    below fails validation on the host first."""
+
+    def __init__(self, shape, ptr=1 << 20, strides=None, itemsize=2):
+        self.shape = shape
+        self._ptr = ptr
+        self._strides = strides or tuple(int(np.prod(shape[i + 1:])) for i in range(len(shape)))
+        self._itemsize = itemsize
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i):
+        return self._strides[i]
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        return self._itemsize
+
+
+def _call(q_shape=(4, 16, 512), fmt=sda.FP8_528, page_size=64, page_stride=None, width=128, H_out=16,
+          extra=False, xfmt=None, plan=None, ws_bytes=None, q_ptr=1 << 20, slot_scale=False, meta=None):
+    T, H, dqk = q_shape
+    q = _FakeTensor(q_shape, ptr=q_ptr)
+    rec = {0: 512, 1: 528, 2: 288, 3: 656}.get(fmt, 512)
+    cache = sda.Cache(_FakeTensor((1,), 1 << 24), 16, page_size, page_stride or page_size * rec, fmt,
+                      _FakeTensor((1,), 1 << 26) if slot_scale else None)
+    lst = sda.SlotList(_FakeTensor((T, width), 1 << 27), width, None)
+    xc = xl = None
+    if extra:
+        xrec = {0: 512, 1: 528, 2: 288, 3: 656}[xfmt]
+        xc = sda.Cache(_FakeTensor((1,), 1 << 28), 16, 64, 64 * xrec, xfmt, None)
+        xl = sda.SlotList(_FakeTensor((T, 64), 1 << 29), 64, None)
+    if plan is None:
+        plan = sda.sda_plan(8, 16, 2, 3)
+    ws = _FakeTensor((ws_bytes if ws_bytes is not None else 1 << 30,), 1 << 30, itemsize=1)
+    out = _FakeTensor((T, H_out, 512), 1 << 31)
+    lse = _FakeTensor((T, H_out), 1 << 32, itemsize=4)
+    ns = None if meta is None else _FakeTensor((T + 1,), 1 << 33)
+    sda.sparse_decode_attn(q, cache, lst, xc, xl, None, 0.05, plan, meta, ns, ws, out, lse, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_shape=(4, 24, 512)), sda.SDA_ERR_UNSUPPORTED),                 # H not supported
+    (dict(q_shape=(4, 16, 576)), sda.SDA_ERR_UNSUPPORTED),                 # fp8_528 holds 512 dims
+    (dict(q_shape=(4, 16, 640)), sda.SDA_ERR_UNSUPPORTED),                 # d_qk
+    (dict(q_shape=(0, 16, 512)), sda.SDA_ERR_INVALID_ARG),                 # T
+    (dict(page_size=48), sda.SDA_ERR_INVALID_ARG),                         # page size not a power of two
+    (dict(page_stride=100), sda.SDA_ERR_INVALID_ARG),                      # page stride too small
+    (dict(page_stride=64 * 528 + 8), sda.SDA_ERR_INVALID_ARG),             # page stride not a multiple of 16
+    (dict(fmt=sda.FP8_SLOTSCALE), sda.SDA_ERR_INVALID_ARG),                # slot scale missing
+    (dict(slot_scale=True), sda.SDA_ERR_INVALID_ARG),                      # slot scale given for fp8_528
+    (dict(fmt=7), sda.SDA_ERR_UNSUPPORTED),                                # unknown format
+    (dict(width=0), sda.SDA_ERR_INVALID_ARG),                              # width
+    (dict(extra=True, xfmt=sda.V32_656), sda.SDA_ERR_UNSUPPORTED),         # extra cache d_qk mismatch
+    (dict(plan=sda.sda_plan(0, 16, 2, 3)), sda.SDA_ERR_INVALID_ARG),       # num_parts
+    (dict(plan=sda.sda_plan(8, 24, 2, 3)), sda.SDA_ERR_UNSUPPORTED),       # heads per group
+    (dict(plan=sda.sda_plan(8, 16, 2, 2)), sda.SDA_ERR_INVALID_ARG),       # precision
+    (dict(ws_bytes=1024), sda.SDA_ERR_WORKSPACE),                          # workspace too small
+    (dict(q_ptr=(1 << 20) + 2), sda.SDA_ERR_INVALID_ARG),                  # q misaligned
+    (dict(meta=True), sda.SDA_ERR_INVALID_ARG),                            # meta without num_splits
+])
+def test_decode_rejects_bad_arguments_on_the_host(kw, status):
+    if kw.get("meta"):
+        # num_splits given, meta missing
+        T = 4
+        plan = sda.sda_plan(8, 16, 2, 3)
+        q = _FakeTensor((T, 16, 512))
+        cache = sda.Cache(_FakeTensor((1,), 1 << 24), 16, 64, 64 * 528, sda.FP8_528, None)
+        lst = sda.SlotList(_FakeTensor((T, 128), 1 << 27), 128, None)
+        with pytest.raises(sda.SdaError) as ei:
+            sda.sparse_decode_attn(q, cache, lst, None, None, None, 0.05, plan, None, _FakeTensor((T + 1,)),
+                                   _FakeTensor((1 << 30,), 1 << 30, itemsize=1), _FakeTensor((T, 16, 512)),
+                                   _FakeTensor((T, 16), itemsize=4), stream=0)
+        assert ei.value.status == status
+        return
+    with pytest.raises(sda.SdaError) as ei:
+        _call(**kw)
+    assert ei.value.status == status
+    assert sda.lib().sda_last_error()
+
+
+def test_extra_cache_without_list_is_rejected():
+    L = sda.lib()
+    T, H = 2, 16
+    cc = sda.sda_cache(1 << 24, 4, 64, sda.FP8_528, 64 * 528, None)
+    cl = sda.sda_list(1 << 27, 128, 128, 0, None)
+    plan = sda.sda_plan(4, 16, 2, 3)
+    rc = L.sda_sparse_decode_attn(1 << 20, 16 * 512, 512, T, H, 512, 512, ctypes.byref(cc), ctypes.byref(cl),
+                                  ctypes.byref(cc), None, None, ctypes.c_float(0.1), ctypes.byref(plan), None, None,
+                                  1 << 30, 1 << 30, 1 << 31, H * 512, 512, 1 << 32, H, None)
+    assert rc == sda.SDA_ERR_INVALID_ARG
+
+
+def test_combine_rejects_bad_arguments():
+    L = sda.lib()
+    assert L.sda_combine_splits(2, 16, 256, 1 << 20, 1 << 21, 1 << 22, None, 1 << 23, 8192, 512, 1 << 24, 16,
+                                None) == sda.SDA_ERR_UNSUPPORTED
+    assert L.sda_combine_splits(2, 16, 512, None, 1 << 21, 1 << 22, None, 1 << 23, 8192, 512, 1 << 24, 16,
+                                None) == sda.SDA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ host scheduler
+
+def _check_schedule(meta, ns, T, n0, n1, P):
+    """Every (token, tile) is covered by exactly one part, in order; split counts match."""
+    tiles = [max(1, -(-a // 64) + -(-b // 64)) for a, b in zip(n0, n1)]
+    seq = [(t, i) for t in range(T) for i in range(tiles[t])]
+    pos = {ti: k for k, ti in enumerate(seq)}
+    covered = []
+    touching = [set() for _ in range(T)]
+    first_k = {}
+    for p in range(P):
+        bt, bi, et, ei, bk = meta[p, :5]
+        b = pos[(bt, bi)] if bt < T else len(seq)
+        e = pos[(et, ei)] if et < T else len(seq)
+        assert b <= e
+        for k in range(b, e):
+            covered.append(seq[k])
+            touching[seq[k][0]].add(p)
+        if b < e:
+            first_k[p] = bk
+    assert covered == seq, "parts must tile the (token, tile) sequence in order"
+    nsplit = [len(s) for s in touching]
+    assert ns[0] == 0 and list(np.diff(ns)) == nsplit
+    assert ns[T] <= T + P
+    for t in range(T):
+        for k, p in enumerate(sorted(touching[t])):
+            bt = meta[p, 0]
+            if bt == t:
+                assert first_k[p] == k
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("P,F", [(1, 2), (7, 0), (64, 2), (256, 5), (1000, 1)])
+def test_host_scheduler_partitions_every_tile_once(seed, P, F):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 300))
+    W, X = 128, int(rng.choice([0, 512, 2048]))
+    lens = rng.integers(-5, W + 20, size=T).astype(np.int32)
+    xl = rng.integers(0, X + 1, size=T).astype(np.int32) if X else None
+    plan = sda.sda_plan(P, 16, F, 3)
+    meta, ns = sda.get_sched_meta_host(T, lens, W, xl, X, plan)
+    n0 = np.clip(lens, 0, W)
+    n1 = np.clip(xl, 0, X) if X else np.zeros(T, dtype=np.int32)
+    _check_schedule(meta, ns, T, n0, n1, P)
+
+
+def test_host_scheduler_balances_cost():
+    T, W = 512, 2048
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, W + 1, size=T).astype(np.int32)
+    plan = sda.sda_plan(256, 16, 2, 3)
+    meta, ns = sda.get_sched_meta_host(T, lens, W, None, 0, plan)
+    tiles = np.maximum(1, -(-lens // 64))
+    total = int((tiles + 2).sum())
+    Q = -(-total // 256)
+    # each part holds at most Q tiles (the quantum), so the busiest part is within one quantum of the mean
+    seq_pos = np.concatenate([[0], np.cumsum(tiles)])
+    for p in range(256):
+        bt, bi, et, ei = meta[p, :4]
+        b = seq_pos[bt] + bi if bt < T else seq_pos[T]
+        e = seq_pos[et] + ei if et < T else seq_pos[T]
+        assert e - b <= Q

@@ -1,0 +1,303 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on an MI355X.
+
+Bar: bf16 output within max-abs 1e-2 and rel-L2 5e-3 of the RNE-bf16 oracle; LSE within 1e-3 absolute
+(infinities exact). Sizes span several 64-row tiles and ragged tails; the five configurations run at
+reduced token counts with the full oracle, and at full size in the benchmark's launch configuration
+on sampled tokens."""
+import copy
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_decode_amd as sda
+import workloads as wl
+from gpu_util import DeviceWorkload, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL_T = {"c1_tiny_swa": 4, "c2_swa_h128": 6, "c3_swa_fp8extra": 12, "c4_swa_nvfp4extra": 6, "c5_topk_v32": 3}
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name", wl.CONFIGS)
+def test_config_parity_reduced_tokens(name, seed):
+    _log(f"[parity] {name} seed={seed} T={SMALL_T[name]}")
+    w = wl.make_workload(name, seed=seed, T=SMALL_T[name])
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    dw = DeviceWorkload(w)
+    out, lse, dec = dw.run()
+    info = compare(out, lse, o_ref, l_ref, what=f"{name}/{seed}")
+    _log(f"  {dec.plan} {info}")
+
+
+@pytest.mark.parametrize("name", wl.CONFIGS)
+def test_config_parity_full_size_sampled(name):
+    """Full-size inputs in the default launch configuration; a sample of tokens checked against the oracle."""
+    _log(f"[parity-full] {name}")
+    w = wl.make_workload(name, seed=0)
+    dw = DeviceWorkload(w)
+    out, lse, dec = dw.run()
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, size=min(w.T, 6), replace=False)]))
+    for t in toks:
+        o_ref, l_ref = oracle.attention(w, tokens=slice(int(t), int(t) + 1), nthreads=8)
+        compare(out[t:t + 1], lse[t:t + 1], o_ref, l_ref, what=f"{name} token {t}")
+    # properties that hold at any size: finite outputs, LSE >= max over sink, outputs bounded by rows
+    assert torch.isfinite(out.float()).all()
+    _log(f"  {dec.plan} checked tokens {list(toks)}")
+
+
+# ------------------------------------------------------------------ plans: results independent of the split
+
+@pytest.mark.parametrize("parts,hb,F", [(1, 16, 2), (3, 16, 0), (17, 32, 5), (64, 16, 1), (1000, 32, 2)])
+def test_any_plan_same_result(parts, hb, F):
+    w = wl.small_workload(3, wl.FP8_528, wl.NVFP4_288, T=9, H=32, width=128, xwidth=300, num_slots=4096,
+                          sink=True, p_invalid=0.05, lens_lo=1)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    dw = DeviceWorkload(w)
+    out, lse, dec = dw.run(plan=sda.sda_plan(parts, hb, F, 3))
+    compare(out, lse, o_ref, l_ref, what=f"plan {parts}/{hb}/{F}")
+
+
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
+def test_heads_and_formats(H, fmt):
+    w = wl.small_workload(10 + H + fmt, fmt, None, T=3, H=H, width=200, num_slots=1024, sink=(H % 32 == 0),
+                          p_invalid=0.1, lens_lo=0)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    out, lse, _ = DeviceWorkload(w).run()
+    compare(out, lse, o_ref, l_ref, what=f"H={H} fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt,xfmt", [(wl.FP8_SLOTSCALE, wl.NVFP4_288), (wl.NVFP4_288, wl.FP8_SLOTSCALE),
+                                      (wl.FP8_528, wl.FP8_SLOTSCALE), (wl.V32_656, wl.V32_656)])
+def test_mixed_list_formats(fmt, xfmt):
+    w = wl.small_workload(40 + fmt, fmt, xfmt, T=5, H=16, width=96, xwidth=160, num_slots=2048, sink=True)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    out, lse, _ = DeviceWorkload(w).run()
+    compare(out, lse, o_ref, l_ref, what=f"mixed {fmt}/{xfmt}")
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _run_cmp(w, what, plan=None, sink="default"):
+    o_ref, l_ref = oracle.attention(w, nthreads=8, sink=sink)
+    dw = DeviceWorkload(w)
+    snk = "default" if isinstance(sink, str) else (None if sink is None else torch.from_numpy(sink).cuda())
+    out, lse, _ = dw.run(plan=plan, sink=snk)
+    return compare(out, lse, o_ref, l_ref, what=what), out, lse
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_lens_zero(sink):
+    w = wl.small_workload(50, wl.FP8_528, wl.FP8_528, T=4, H=16, width=64, xwidth=64, sink=sink)
+    w.lst.lens[:] = 0
+    w.xlst.lens[:] = 0
+    _, out, lse = _run_cmp(w, "lens=0")
+    assert torch.all(out == 0)
+
+
+def test_all_slots_invalid():
+    w = wl.small_workload(51, wl.NVFP4_288, None, T=3, H=32, width=130, sink=True)
+    w.lst.idx[:] = -1
+    w.lst.lens[:] = 130
+    _run_cmp(w, "all -1")
+
+
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
+def test_single_valid_slot_returns_its_row(fmt):
+    w = wl.small_workload(52 + fmt, fmt, None, T=4, H=32, width=100, num_slots=512)
+    w.lst.idx[:] = -1
+    for t in range(w.T):
+        w.lst.idx[t, (37 * t) % 100] = 7 + 100 * t
+        w.lst.lens[t] = 100
+    _run_cmp(w, f"single slot fmt {fmt}")
+
+
+def test_out_of_range_and_negative_slots():
+    w = wl.small_workload(56, wl.FP8_528, wl.FP8_528, T=4, H=16, width=128, xwidth=128, num_slots=1024, sink=True)
+    rng = np.random.default_rng(0)
+    for L in (w.lst, w.xlst):
+        m = rng.random(L.idx.shape) < 0.2
+        L.idx[m] = rng.choice([1024, 1025, 1 << 30, -2, -1 << 31], size=int(m.sum())).astype(np.int32)
+    _run_cmp(w, "out of range")
+
+
+def test_lens_beyond_width_and_negative():
+    w = wl.small_workload(57, wl.FP8_SLOTSCALE, wl.NVFP4_288, T=6, H=16, width=70, xwidth=130, sink=True)
+    w.lst.lens[:] = [1000, -3, 70, 0, 69, 1 << 30]
+    w.xlst.lens[:] = [-1, 130, 131, 65, 64, 1]
+    _run_cmp(w, "lens clamp")
+
+
+def test_page_stride_padding_and_small_pages():
+    w = wl.small_workload(58, wl.FP8_528, wl.NVFP4_288, T=4, H=16, width=128, xwidth=128, num_slots=1024,
+                          page_size=16, pad_bytes=272, sink=True)
+    _run_cmp(w, "padded pages")
+
+
+def test_row_stride_longer_than_width():
+    w = wl.small_workload(59, wl.FP8_528, wl.FP8_528, T=4, H=16, width=90, xwidth=70, row_stride_extra=13)
+    _run_cmp(w, "row stride")
+
+
+def test_duplicate_slots():
+    w = wl.small_workload(60, wl.FP8_528, None, T=3, H=16, width=64, num_slots=256)
+    w.lst.idx[:, :] = -1
+    w.lst.idx[:, 3] = 11
+    w.lst.idx[:, 40] = 11
+    w.lst.idx[:, 41] = 200
+    w.lst.lens[:] = 64
+    _run_cmp(w, "duplicates")
+
+
+def test_sink_infinities():
+    w = wl.small_workload(61, wl.FP8_528, None, T=3, H=16, width=64)
+    _run_cmp(w, "sink -inf", sink=np.full(16, -np.inf, dtype=np.float32))
+    _, out, lse = _run_cmp(w, "sink +inf", sink=np.full(16, np.inf, dtype=np.float32))
+    assert torch.all(out == 0)
+
+
+def test_large_scores_and_rescaling():
+    """Scores spread over a wide range force the running max to move across tiles."""
+    w = wl.small_workload(62, wl.FP8_528, wl.FP8_528, T=3, H=16, width=256, xwidth=256, sink=True, lens_lo=200)
+    w2 = copy.deepcopy(w)
+    qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float() * 8.0
+    w2.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    _run_cmp(w2, "wide scores")
+
+
+def test_strided_q_and_out():
+    w = wl.small_workload(63, wl.FP8_528, None, T=5, H=32, width=100, sink=True)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    dw = DeviceWorkload(w)
+    qbig = torch.zeros((w.T, w.H + 3, 512 + 64), dtype=torch.bfloat16, device="cuda")
+    qbig[:, :w.H, :512] = dw.q
+    q = qbig[:, :w.H, :512]
+    obig = torch.full((w.T, w.H + 1, 512 + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = obig[:, :w.H, :512]
+    lbig = torch.full((w.T, w.H + 5), 7.0, dtype=torch.float32, device="cuda")
+    lse = lbig[:, :w.H]
+    dw.run(q=q, out=out, lse=lse)
+    compare(out, lse, o_ref, l_ref, what="strided")
+    assert torch.all(obig[:, w.H:, :] == 7.0) and torch.all(obig[:, :, 512:] == 7.0)
+    assert torch.all(lbig[:, w.H:] == 7.0)
+
+
+def test_precision_one_term_on_many_rows():
+    """The faster single-term P mode on a top-k shape with many rows per token."""
+    w = wl.make_workload("c5_topk_v32", seed=4, T=2)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width)
+    plan.precision = 1
+    out, lse, _ = DeviceWorkload(w).run(plan=plan)
+    compare(out, lse, o_ref, l_ref, what="precision 1")
+
+
+# ------------------------------------------------------------------ decode tables on the GPU
+
+def test_every_e4m3_code_decodes_exactly():
+    """Rows that hold every finite e4m3 code; a single valid slot returns its row exactly."""
+    rng = np.random.default_rng(5)
+    c = wl.make_cache(rng, wl.FP8_528, 64, page_size=64)
+    codes = np.array([x for x in range(256) if x not in (0x7F, 0xFF)], dtype=np.uint8)
+    for s in range(4):
+        rec = c.data[s * 528:(s + 1) * 528]
+        row = np.concatenate([codes, codes])[:512]
+        rec[:512] = np.roll(row, 37 * s)
+        rec[512:528] = np.array([1.0, 0.5, 2.0, 0.75], dtype=np.float32).view(np.uint8)
+    q = wl.make_q(rng, 4, 16, 512)
+    idx = np.full((4, 8), -1, dtype=np.int32)
+    idx[:, 2] = np.arange(4)
+    lst = wl.SlotList(idx, 8, np.full(4, 8, dtype=np.int32))
+    w = wl.Workload("e4m3 table", 4, 16, 512, 512, q, c, lst, None, None, None, 0.05)
+    _, out, _ = _run_cmp(w, "e4m3 table")
+    for t in range(4):
+        ref = oracle.decode_slot(c, t)
+        assert np.array_equal(out[t, 0].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
+
+
+def test_every_e2m1_code_and_block_scale():
+    rng = np.random.default_rng(6)
+    c = wl.make_cache(rng, wl.NVFP4_288, 64, page_size=64)
+    for s in range(4):
+        rec = c.data[s * 288:(s + 1) * 288]
+        rec[:256] = (np.arange(256) + 17 * s) % 256
+        rec[256:288] = rng.choice([x for x in range(0x08, 0x78)], size=32)
+    q = wl.make_q(rng, 4, 16, 512)
+    idx = np.full((4, 8), -1, dtype=np.int32)
+    idx[:, 5] = np.arange(4)
+    lst = wl.SlotList(idx, 8, np.full(4, 8, dtype=np.int32))
+    w = wl.Workload("e2m1 table", 4, 16, 512, 512, q, c, lst, None, None, None, 0.05)
+    _, out, _ = _run_cmp(w, "e2m1 table")
+    for t in range(4):
+        ref = oracle.decode_slot(c, t)
+        assert np.array_equal(out[t, 3].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
+
+
+# ------------------------------------------------------------------ scheduler and combine through the ABI
+
+@pytest.mark.parametrize("P,F", [(1, 2), (256, 2), (513, 0), (4096, 5)])
+def test_device_scheduler_matches_host(P, F):
+    rng = np.random.default_rng(P)
+    T = 700
+    lens = rng.integers(-3, 140, size=T).astype(np.int32)
+    xl = rng.integers(0, 2049, size=T).astype(np.int32)
+    plan = sda.sda_plan(P, 16, F, 3)
+    meta_h, ns_h = sda.get_sched_meta_host(T, lens, 128, xl, 2048, plan)
+    lst = sda.SlotList(torch.zeros((T, 128), dtype=torch.int32, device="cuda"), 128, torch.from_numpy(lens).cuda())
+    xlst = sda.SlotList(torch.zeros((T, 2048), dtype=torch.int32, device="cuda"), 2048, torch.from_numpy(xl).cuda())
+    meta = torch.full((P, 8), -7, dtype=torch.int32, device="cuda")
+    ns = torch.full((T + 1,), -7, dtype=torch.int32, device="cuda")
+    sda.get_sched_meta(T, lst, xlst, plan, meta, ns)
+    torch.cuda.synchronize()
+    assert np.array_equal(meta.cpu().numpy(), meta_h)
+    assert np.array_equal(ns.cpu().numpy(), ns_h)
+
+
+def test_combine_splits_against_oracle_merge():
+    w = wl.small_workload(70, wl.FP8_528, None, T=5, H=16, width=192, num_slots=2048, sink=True, lens_lo=100)
+    H = w.H
+    nparts = [2, 3, 2, 4, 5]
+    o_parts, l_parts, refs = [], [], []
+    rng = np.random.default_rng(0)
+    for t in range(w.T):
+        tw = copy.deepcopy(w)
+        tw.T = 1
+        tw.q = w.q[t:t + 1]
+        tw.lst = wl.SlotList(w.lst.idx[t:t + 1].copy(), w.lst.width, w.lst.lens[t:t + 1].copy())
+        owner = rng.integers(0, nparts[t], size=w.lst.width)
+        for p in range(nparts[t]):
+            pw = copy.deepcopy(tw)
+            pw.lst.idx[0, owner != p] = -1
+            o, l = oracle.attention(pw, sink=None)
+            o_parts.append(o[0])
+            l_parts.append(l[0])
+        refs.append(oracle.attention(tw))
+    ns = np.concatenate([[0], np.cumsum(nparts)]).astype(np.int32)
+    o_acc = torch.from_numpy(np.array(o_parts, dtype=np.float32)).cuda()
+    l_acc = torch.from_numpy(np.array(l_parts, dtype=np.float32)).cuda()
+    out = torch.zeros((w.T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((w.T, H), dtype=torch.float32, device="cuda")
+    sda.combine_splits(o_acc, l_acc, torch.from_numpy(ns).cuda(), torch.from_numpy(w.sink).cuda(), out, lse)
+    torch.cuda.synchronize()
+    o_ref = np.concatenate([r[0] for r in refs])
+    l_ref = np.concatenate([r[1] for r in refs])
+    compare(out, lse, o_ref, l_ref, what="combine")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = wl.make_workload("c4_swa_nvfp4extra", seed=2, T=40)
+    dw = DeviceWorkload(w)
+    o1, l1, _ = dw.run()
+    o2, l2, _ = dw.run()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
