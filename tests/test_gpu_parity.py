@@ -167,13 +167,32 @@ def test_sink_infinities():
     assert torch.all(out == 0)
 
 
-def test_large_scores_and_rescaling():
-    """Scores spread over a wide range force the running max to move across tiles."""
+def test_rescale_path_with_rows_sorted_by_score():
+    """Rows ordered by increasing score make the running max move up by more than the rescale
+    threshold from tile to tile (moderate logits, the strict bar)."""
+    w = wl.small_workload(64, wl.FP8_528, None, T=3, H=16, width=1024, num_slots=4096, sink=True, lens_lo=1024,
+                          p_invalid=0.0)
+    qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float() * 1.5
+    w.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = qf.double().numpy()
+    for t in range(w.T):
+        k = np.array([oracle.decode_slot(w.cache, int(s)) for s in w.lst.idx[t]])
+        z = k @ q[t, 0]
+        w.lst.idx[t] = w.lst.idx[t][np.argsort(z)]
+    _run_cmp(w, "sorted rows")
+
+
+def test_extreme_logits():
+    """Scores of magnitude ~30: fp32 score rounding (ulp(30) ~ 2e-6) can flip the bf16 rounding of an
+    output element that sits on a rounding boundary; such flips (one ulp) are counted, not hidden."""
     w = wl.small_workload(62, wl.FP8_528, wl.FP8_528, T=3, H=16, width=256, xwidth=256, sink=True, lens_lo=200)
     w2 = copy.deepcopy(w)
     qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float() * 8.0
     w2.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    _run_cmp(w2, "wide scores")
+    o_ref, l_ref = oracle.attention(w2, nthreads=8)
+    out, lse, _ = DeviceWorkload(w2).run()
+    info = compare(out, lse, o_ref, l_ref, what="extreme logits", allow_ulp_flips=True)
+    _log(f"  extreme logits: {info}")
 
 
 def test_strided_q_and_out():
@@ -212,7 +231,7 @@ def test_every_e4m3_code_decodes_exactly():
     codes = np.array([x for x in range(256) if x not in (0x7F, 0xFF)], dtype=np.uint8)
     for s in range(4):
         rec = c.data[s * 528:(s + 1) * 528]
-        row = np.concatenate([codes, codes])[:512]
+        row = np.resize(codes, 512)
         rec[:512] = np.roll(row, 37 * s)
         rec[512:528] = np.array([1.0, 0.5, 2.0, 0.75], dtype=np.float32).view(np.uint8)
     q = wl.make_q(rng, 4, 16, 512)
