@@ -166,6 +166,22 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
                            void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                            void* stream);
 
+/* The decode kernel alone (FlashMLA sparse_decode.h: impl->run, before the combine): same arguments
+ * and checks as sda_sparse_decode_attn, but meta and num_splits are required and no combine runs.
+ * Tokens touched by a single part get their final out/lse rows; the others get normalized fp32
+ * partials in the workspace (o_accum at offset 0, lse_accum after it, as laid out by
+ * sda_workspace_bytes) for a later sda_combine_splits. */
+int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                      const sda_cache* cache /*host*/, const sda_list* list /*host*/,
+                      const sda_cache* extra_cache /*host, nullable*/, const sda_list* extra_list /*host, nullable*/,
+                      const float* attn_sink, float scale, const sda_plan* plan /*host*/,
+                      const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                      void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                      void* stream);
+
+/* Host only. Byte offsets of lse_accum in the workspace of this plan (o_accum starts at 0). */
+size_t sda_workspace_lse_offset(int T, int H, int d_v, const sda_plan* plan /*host*/);
+
 /* LSE merge of split partials (FlashMLA sparse_decode.h: run_flash_mla_combine_kernel; the merge of
  * vLLM swapab_decode_attn step 9 with the sink folded in once). For every token t with
  * n_t = num_splits[t+1] - num_splits[t] >= 2: with s = num_splits[t] + k for k < n_t,

@@ -21,7 +21,7 @@ META_INTS = 8
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED_SYMBOLS = ("sda_make_plan", "sda_workspace_bytes", "sda_get_sched_meta", "sda_get_sched_meta_host",
-                    "sda_sparse_decode_attn",
+                    "sda_sparse_decode_attn", "sda_decode_splits", "sda_workspace_lse_offset",
                     "sda_combine_splits", "sda_status_string", "sda_last_error", "sda_record_bytes",
                     "sda_format_dims")
 
@@ -73,6 +73,9 @@ def lib():
                                              ctypes.POINTER(sda_list), ctypes.POINTER(sda_cache),
                                              ctypes.POINTER(sda_list), vp, ctypes.c_float, ctypes.POINTER(sda_plan),
                                              vp, vp, vp, sz, vp, i64, i64, vp, i64, vp]
+        L.sda_decode_splits.argtypes = L.sda_sparse_decode_attn.argtypes
+        L.sda_workspace_lse_offset.argtypes = [i32, i32, i32, ctypes.POINTER(sda_plan)]
+        L.sda_workspace_lse_offset.restype = sz
         L.sda_combine_splits.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp]
         L.sda_status_string.argtypes = [i32]
         L.sda_status_string.restype = ctypes.c_char_p
@@ -155,20 +158,38 @@ def get_sched_meta_host(T: int, lens, width: int, extra_lens, extra_width: int, 
     return meta, ns
 
 
-def sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
-                       attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, out, lse, stream=None):
-    """q [T, H, d_qk] bf16, out [T, H, 512] bf16, lse [T, H] fp32 (all device tensors, strided rows allowed)."""
+def _decode_call(fn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits, workspace,
+                 out, lse, stream):
     T, H, d_qk = q.shape
     d_v = out.shape[-1]
     cc, cl = cache.c(), lst.c()
     xc = extra_cache.c() if extra_cache is not None else None
     xl = extra_lst.c() if extra_lst is not None else None
-    _check(lib().sda_sparse_decode_attn(
+    _check(fn(
         _ptr(q), q.stride(0), q.stride(1), T, H, d_qk, d_v, ctypes.byref(cc), ctypes.byref(cl),
         ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
         _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)))
+
+
+def sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
+                       attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, out, lse, stream=None):
+    """Whole op: (scheduler if meta is None) + decode + combine.
+    q [T, H, d_qk] bf16, out [T, H, 512] bf16, lse [T, H] fp32 (device tensors, strided rows allowed)."""
+    _decode_call(lib().sda_sparse_decode_attn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta,
+                 num_splits, workspace, out, lse, stream)
+
+
+def decode_splits(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
+                  attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, out, lse, stream=None):
+    """The decode kernel only (final rows for unsplit tokens, partials in the workspace for the others)."""
+    _decode_call(lib().sda_decode_splits, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta,
+                 num_splits, workspace, out, lse, stream)
+
+
+def workspace_lse_offset(T: int, H: int, d_v: int, plan: sda_plan) -> int:
+    return int(lib().sda_workspace_lse_offset(T, H, d_v, ctypes.byref(plan)))
 
 
 def combine_splits(o_accum, lse_accum, num_splits, attn_sink, out, lse, stream=None):

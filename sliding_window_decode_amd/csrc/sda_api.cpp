@@ -269,12 +269,14 @@ int sda_get_sched_meta_host(int T, const int32_t* lens, int width, const int32_t
   return SDA_OK;
 }
 
-int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
-                           const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
-                           const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
-                           const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
-                           void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
-                           void* stream) {
+namespace {
+
+// Checks shared by sda_sparse_decode_attn and sda_decode_splits.
+int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                      const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                      const sda_list* extra_list, const sda_plan* plan, const int32_t* meta, const int32_t* num_splits,
+                      void* workspace, size_t workspace_bytes, void* out, int64_t out_stride_t, int64_t out_stride_h,
+                      float* lse, int64_t lse_stride_t) {
   if (!q || !out || !lse) return fail(SDA_ERR_INVALID_ARG, "q, out and lse are required");
   if (T < 1) return fail(SDA_ERR_INVALID_ARG, "T must be >= 1");
   if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
@@ -300,18 +302,14 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
   if (!workspace || !aligned(workspace, 256)) return fail(SDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < wl.total) return fail(SDA_ERR_WORKSPACE, "workspace smaller than sda_workspace_bytes()");
+  return SDA_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  if (!meta) {
-    int32_t* m = (int32_t*)(ws + wl.meta);
-    int32_t* ns = (int32_t*)(ws + wl.num_splits);
-    hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
-    if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
-    meta = m;
-    num_splits = ns;
-  }
-
+sda::DecodeParams decode_params(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
+                                const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                                const sda_list* extra_list, const float* attn_sink, float scale, const int32_t* meta,
+                                const int32_t* num_splits, char* ws, const WorkspaceLayout& wl, void* out,
+                                int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t) {
   sda::DecodeParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const uint16_t*)q;
@@ -336,13 +334,16 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
   p.T = T;
   p.H = H;
   p.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision, st);
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return p;
+}
 
+sda::CombineParams combine_params(int T, int H, const float* o_acc, const float* lse_acc, const int32_t* num_splits,
+                                  const float* attn_sink, void* out, int64_t out_stride_t, int64_t out_stride_h,
+                                  float* lse, int64_t lse_stride_t) {
   sda::CombineParams c;
   memset(&c, 0, sizeof(c));
-  c.o_acc = p.o_acc;
-  c.lse_acc = p.lse_acc;
+  c.o_acc = o_acc;
+  c.lse_acc = lse_acc;
   c.num_splits = num_splits;
   c.sink = attn_sink;
   c.out = (uint16_t*)out;
@@ -352,7 +353,66 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
   c.l_st = lse_stride_t;
   c.T = T;
   c.H = H;
-  e = sda::launch_combine(c, st);
+  return c;
+}
+
+}  // namespace
+
+size_t sda_workspace_lse_offset(int T, int H, int d_v, const sda_plan* plan) {
+  if (!plan || T < 1 || H < 1 || d_v < 1 || plan->num_parts < 1) return 0;
+  return layout_of(T, H, d_v, plan->num_parts).lse_acc;
+}
+
+int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                      const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                      const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                      const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                      void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                      void* stream) {
+  int rc = check_decode_args(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, plan,
+                             meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h, lse,
+                             lse_stride_t);
+  if (rc) return rc;
+  if (!meta) return fail(SDA_ERR_INVALID_ARG, "sda_decode_splits needs meta and num_splits");
+  const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
+  const sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
+                                            attn_sink, scale, meta, num_splits, (char*)workspace, wl, out,
+                                            out_stride_t, out_stride_h, lse, lse_stride_t);
+  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return SDA_OK;
+}
+
+int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                           const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                           const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                           const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                           void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                           void* stream) {
+  int rc = check_decode_args(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, plan,
+                             meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h, lse,
+                             lse_stride_t);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
+  if (!meta) {
+    int32_t* m = (int32_t*)(ws + wl.meta);
+    int32_t* ns = (int32_t*)(ws + wl.num_splits);
+    hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
+    if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
+    meta = m;
+    num_splits = ns;
+  }
+  const sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
+                                            attn_sink, scale, meta, num_splits, ws, wl, out, out_stride_t,
+                                            out_stride_h, lse, lse_stride_t);
+  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision, st);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  e = sda::launch_combine(combine_params(T, H, p.o_acc, p.lse_acc, num_splits, attn_sink, out, out_stride_t,
+                                         out_stride_h, lse, lse_stride_t),
+                          st);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return SDA_OK;
 }
@@ -366,19 +426,8 @@ int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float*
   if (!aligned(o_accum, 16) || !aligned(out, 8) || out_stride_h % 4 || out_stride_t % 4 || out_stride_h < d_v)
     return fail(SDA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, out 8-byte aligned with strides in 4s");
   if (lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
-  sda::CombineParams c;
-  memset(&c, 0, sizeof(c));
-  c.o_acc = o_accum;
-  c.lse_acc = lse_accum;
-  c.num_splits = num_splits;
-  c.sink = attn_sink;
-  c.out = (uint16_t*)out;
-  c.o_st = out_stride_t;
-  c.o_sh = out_stride_h;
-  c.lse = lse;
-  c.l_st = lse_stride_t;
-  c.T = T;
-  c.H = H;
+  const sda::CombineParams c = combine_params(T, H, o_accum, lse_accum, num_splits, attn_sink, out, out_stride_t,
+                                             out_stride_h, lse, lse_stride_t);
   hipError_t e = sda::launch_combine(c, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return SDA_OK;
