@@ -28,7 +28,8 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "sliding_window_decode_amd", "csrc", "sda_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
+               for f in ("sda_decode.hip", "sda_sched.hip", "sda_device.h", "sda_internal.h")]
 
 
 def log(*a):
@@ -53,8 +54,11 @@ def algorithmic_work(w):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str, sha: str):

@@ -188,12 +188,12 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
   if (d_qk != 512 && d_qk != 576) return fail(SDA_ERR_UNSUPPORTED, "d_qk must be 512 or 576");
   if (num_cus <= 0) num_cus = 256;
-  // Heads per workgroup: the largest group that still gives every CU a workgroup by tokens x head
-  // groups alone; smaller groups re-read the token's rows (from L2) but need no split partials.
-  int hb = H < 32 ? H : 32;
-  while (hb > 16 && (int64_t)T * (H / hb) < num_cus) hb /= 2;
+  // Heads per workgroup: 16 (two workgroups fit per CU); the other head groups of a part re-read the
+  // token's rows, mostly from L2 (a part's head groups land on the same XCD when num_parts % 8 == 0).
+  const int hb = 16;
   const int groups = H / hb;
   int parts = (2 * num_cus) / groups;
+  if (parts < 8) parts = 8;
   if (parts < 1) parts = 1;
   plan->num_parts = parts;
   plan->heads_per_group = hb;

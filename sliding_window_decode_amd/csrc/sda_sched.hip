@@ -1,0 +1,166 @@
+// sda_sched.hip -- the split scheduler and the LSE combine kernel.
+//
+// Scheduler (FlashMLA sparse_decode.h: get_decoding_sched_meta, DecodeImplMeta): every token costs
+// max(1, ceil(n_main/64) + ceil(n_extra/64)) tiles plus a fixed overhead F; the concatenated
+// (token, tile) sequence is cut into num_parts contiguous parts of equal cost (see sda_internal.h).
+// Combine (FlashMLA run_flash_mla_combine_kernel; vLLM swapab_decode_attn step 9): LSE-weighted sum
+// of the normalized partials of every split token, the sink folded into the denominator once.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sda_device.h"
+#include "sda_internal.h"
+
+namespace sda {
+
+// Inclusive prefix sum over the block (wave shuffles, one barrier for the wave totals).
+__device__ int block_incl_scan(int v, int* wave_tot, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = wave_tot[w];
+    before += (w < wave) ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  total = all;
+  return v + before;
+}
+
+__global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
+  __shared__ int wave_tot[16];
+  const int tid = threadIdx.x;
+  const int NT = blockDim.x;
+  int local = 0;
+  for (int t = tid; t < p.T; t += NT) {
+    const int n0 = clamp_len(p.lens[0], p.width[0], t);
+    const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
+    local += token_tiles(n0, n1) + p.F;
+  }
+  int total = 0;
+  (void)block_incl_scan(local, wave_tot, total);
+  const int Q = (int)part_quantum(total, p.num_parts);
+  int carry = 0, split_carry = 0;
+  for (int base = 0; base < p.T; base += NT) {
+    const int t = base + tid;
+    int nt = 0, cost = 0;
+    if (t < p.T) {
+      const int n0 = clamp_len(p.lens[0], p.width[0], t);
+      const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
+      nt = token_tiles(n0, n1);
+      cost = nt + p.F;
+    }
+    int chunk_cost = 0;
+    const int cum = carry + block_incl_scan(cost, wave_tot, chunk_cost) - cost;  // cost-axis start of t
+    int nsplit = 0, pos0 = 0, p0 = 0, p1 = 0;
+    if (t < p.T) {
+      pos0 = cum + p.F;  // position of the token's first tile
+      p0 = pos0 / Q;
+      p1 = (pos0 + nt - 1) / Q;
+      nsplit = p1 - p0 + 1;
+    }
+    int chunk_splits = 0;
+    const int sincl = block_incl_scan(nsplit, wave_tot, chunk_splits);
+    if (t < p.T) {
+      p.num_splits[t] = split_carry + sincl - nsplit;
+      const int prev_last = (cum == 0) ? -1 : (cum - 1) / Q;  // part of the previous token's last tile
+      for (int pp = prev_last + 1; pp <= p1; ++pp) {
+        const int bi = pp * Q - pos0 > 0 ? pp * Q - pos0 : 0;
+        int32_t* m = p.meta + (int64_t)pp * SDA_META_INTS;
+        m[0] = t;
+        m[1] = bi;
+        m[4] = (pp >= p0) ? pp - p0 : 0;
+        m[5] = 0;
+        m[6] = 0;
+        m[7] = 0;
+        if (pp > 0) {
+          int32_t* mp = p.meta + (int64_t)(pp - 1) * SDA_META_INTS;
+          mp[2] = t;
+          mp[3] = bi;
+        }
+      }
+    }
+    carry += chunk_cost;
+    split_carry += chunk_splits;
+  }
+  const int last = (total - 1) / Q;  // part of the very last tile
+  for (int pp = last + 1 + tid; pp < p.num_parts; pp += NT) {
+    int32_t* m = p.meta + (int64_t)pp * SDA_META_INTS;
+    m[0] = p.T; m[1] = 0; m[2] = p.T; m[3] = 0; m[4] = 0; m[5] = 0; m[6] = 0; m[7] = 0;
+  }
+  if (tid == 0) {
+    int32_t* m = p.meta + (int64_t)last * SDA_META_INTS;
+    m[2] = p.T;
+    m[3] = 0;
+    p.num_splits[p.T] = split_carry;
+  }
+}
+
+// One workgroup per (token, block of 16 heads); thread (head h = tid / 16, 32 dims from 32 * (tid % 16)).
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int t = blockIdx.x;
+  const int s0 = p.num_splits[t];
+  const int n = p.num_splits[t + 1] - s0;
+  if (n < 2) return;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y * 16 + (tid >> 4);
+  const int d0 = 32 * (tid & 15);
+  const bool has_sink = p.sink != nullptr;
+  const float sk = has_sink ? p.sink[h] : kNegInf;
+  float M = sk;
+  for (int k = 0; k < n; ++k) M = fmaxf(M, p.lse_acc[(int64_t)(s0 + k) * p.H + h]);
+  uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + d0;
+  if (M == kNegInf || M == kPosInf) {
+    for (int e = 0; e < 32; e += 8) *(u32x4*)(orow + e) = u32x4{0u, 0u, 0u, 0u};
+    if ((tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = M;
+    return;
+  }
+  float den = has_sink ? expf(sk - M) : 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n; ++k) {
+    const float lk = p.lse_acc[(int64_t)(s0 + k) * p.H + h];
+    if (lk == kNegInf) continue;
+    const float w = expf(lk - M);
+    den += w;
+    const f32x4* src = (const f32x4*)(p.o_acc + ((int64_t)(s0 + k) * p.H + h) * kDv + d0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += w * src[e];
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4& a = acc[e + (q >> 1)];
+      const int k = (q & 1) * 2;
+      o[q] = (uint32_t)f32_to_bf16_bits(a[k] * inv) | ((uint32_t)f32_to_bf16_bits(a[k + 1] * inv) << 16);
+    }
+    *(u32x4*)(orow + 4 * e) = o;
+  }
+  if ((tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = M + logf(den);
+}
+
+hipError_t launch_sched(const SchedParams& p, hipStream_t stream) {
+  const int threads = p.T >= 1024 ? 1024 : ((p.T + 63) / 64) * 64;
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(threads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sda

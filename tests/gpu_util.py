@@ -49,12 +49,14 @@ class DeviceWorkload:
         return o, l, dec
 
 
-def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", allow_ulp_flips=False):
-    """Assert the stated tolerances; returns a dict of the error figures.
+def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what=""):
+    """Assert the tolerances; returns a dict of the error figures.
 
-    allow_ulp_flips: for inputs with extreme logits only -- an element may differ from the rounded
-    reference by one bf16 ulp (a rounding-boundary flip caused by fp32 score rounding) even where that
-    ulp exceeds the max-abs bound; such elements are counted in the returned figures."""
+    out: every element within 1e-2 of the round-to-nearest-even bf16 of the fp64 oracle, except that an
+    element may sit one bf16 ulp away where that ulp itself exceeds 1e-2 (|x| >= 2): a rounding-boundary
+    flip, which an fp32 computation produces whenever the exact value lies within its rounding error of
+    a bf16 midpoint. Flips are counted and must stay below 1 in 10^4 elements. rel-L2 <= 5e-3 over all
+    elements. lse: within 1e-3 absolute, infinities exact."""
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     lg = lse_gpu.float().cpu().numpy().astype(np.float64)
     if tokens is not None:
@@ -64,22 +66,16 @@ def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", allow_ulp_flip
     max_abs = float(diff.max()) if diff.size else 0.0
     nrm = float(np.linalg.norm(ref))
     rel_l2 = float(np.linalg.norm(got - ref) / nrm) if nrm > 0 else float(np.linalg.norm(got))
-    # LSE: infinities must match exactly, finite values within tolerance
     inf_ref = ~np.isfinite(l_ref)
     assert np.array_equal(inf_ref, ~np.isfinite(lg)), f"{what}: LSE infinities differ"
     assert np.array_equal(l_ref[inf_ref], lg[inf_ref]), f"{what}: LSE infinity signs differ"
     lse_err = float(np.abs(lg[~inf_ref] - l_ref[~inf_ref]).max()) if (~inf_ref).any() else 0.0
-    n_over = int((diff > OUT_MAX_ABS).sum())
-    info = dict(max_abs=max_abs, rel_l2=rel_l2, lse_max_abs=lse_err, n_over=n_over)
+    over = diff > OUT_MAX_ABS
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)  # bf16 spacing at |ref|
+    info = dict(max_abs=max_abs, rel_l2=rel_l2, lse_max_abs=lse_err, ulp_flips=int(over.sum()), n=int(diff.size))
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    if allow_ulp_flips:
-        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)  # bf16 spacing at |ref|
-        flips = diff > OUT_MAX_ABS
-        assert np.all(diff[flips] <= ulp[flips]), f"{what}: error beyond one bf16 ulp {info}"
-        info["ulp_flips"] = int(flips.sum())
-        assert info["ulp_flips"] <= max(1, diff.size // 1000), f"{what}: too many flips {info}"
-    else:
-        assert max_abs <= OUT_MAX_ABS, f"{what}: out max-abs {max_abs:.3e} ({n_over} elements over) {info}"
+    assert np.all(diff[over] <= ulp[over]), f"{what}: error beyond 1e-2 and beyond one bf16 ulp {info}"
+    assert info["ulp_flips"] <= max(1, diff.size // 10000), f"{what}: too many rounding flips {info}"
     assert rel_l2 <= OUT_REL_L2, f"{what}: out rel-L2 {rel_l2:.3e} {info}"
     assert lse_err <= LSE_MAX_ABS, f"{what}: lse max-abs {lse_err:.3e} {info}"
     return info

@@ -1,6 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle on an MI355X.
 
-Bar: bf16 output within max-abs 1e-2 and rel-L2 5e-3 of the RNE-bf16 oracle; LSE within 1e-3 absolute
+Bar (tests/gpu_util.compare): bf16 output within max-abs 1e-2 of the RNE-bf16 oracle, up to counted
+one-ulp rounding-boundary flips where one ulp exceeds 1e-2; rel-L2 5e-3; LSE within 1e-3 absolute
 (infinities exact). Sizes span several 64-row tiles and ragged tails; the five configurations run at
 reduced token counts with the full oracle, and at full size in the benchmark's launch configuration
 on sampled tokens."""
@@ -191,7 +192,7 @@ def test_extreme_logits():
     w2.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     o_ref, l_ref = oracle.attention(w2, nthreads=8)
     out, lse, _ = DeviceWorkload(w2).run()
-    info = compare(out, lse, o_ref, l_ref, what="extreme logits", allow_ulp_flips=True)
+    info = compare(out, lse, o_ref, l_ref, what="extreme logits")
     _log(f"  extreme logits: {info}")
 
 
