@@ -96,7 +96,8 @@ __device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
 }
 
 template <int DQK, int NH2, int NTERM>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH2 == 1 ? 3 : 1)))
+void decode_kernel(DecodeParams p) {
   constexpr int RS = DecodeSmem<DQK, NH2>::RS;
   constexpr bool kRope = DQK == 576;
   __shared__ DecodeSmem<DQK, NH2> sm;
@@ -106,25 +107,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int G = lane >> 4, li = lane & 15;
   const int h0 = blockIdx.y * (16 * NH2);
 
+  const ListDev lst0 = p.lst[0];
+  const ListDev lst1 = p.lst[p.nlists > 1 ? 1 : 0];
+  auto LD = [&](int L) -> const ListDev& { return L ? lst1 : lst0; };
   const int32_t* mt = p.meta + (int64_t)blockIdx.x * SDA_META_INTS;
   const int bt = mt[0], bi = mt[1], et = mt[2], ei = mt[3], bk = mt[4];
   if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
 
   // ---- per-lane LDS bases (rows of a sub-tile start at multiples of 8, so a lane's swizzle term is
   // the same for every row it touches; every access below is base + a compile-time offset)
-  const char* kb[2];
-  const char* kr;
-  const char* vb[4];
+  uint32_t kb[2], kr, vb[4];  // byte offsets into sm.tile
   {
     const int f = ((li & 3) << 1) | ((li >> 2) & 1);  // K operand rows li (+16 rb)
-    kb[0] = sm.tile + li * RS + 256 * w + 16 * (G ^ f);
-    kb[1] = sm.tile + li * RS + 256 * w + 16 * ((4 + G) ^ f);
-    kr = sm.tile + li * RS + 16 * (64 + ((4 * (w & 1) + G) ^ f));
+    kb[0] = li * RS + 256 * w + 16 * (G ^ f);
+    kb[1] = li * RS + 256 * w + 16 * ((4 + G) ^ f);
+    kr = li * RS + 16 * (64 + ((4 * (w & 1) + G) ^ f));
     const int rv = 4 * G + (li >> 2);  // V operand rows rv .. rv + 3 (+16)
     const int fv = ((rv & 3) << 1) | ((rv >> 2) & 1);
     const int cb = (li & 3) >> 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) vb[q] = sm.tile + rv * RS + 256 * w + 16 * ((2 * q + cb) ^ fv) + 8 * (li & 1);
+    for (int q = 0; q < 4; ++q) vb[q] = rv * RS + 256 * w + 16 * ((2 * q + cb) ^ fv) + 8 * (li & 1);
   }
 
   // ---- slot ids -> addresses (threads 0..31, one row each)
@@ -133,12 +135,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     pf_sid = -1;
     if (!it.end && tid < KT) {
       const int pos = it.pos0 + tid;
-      if (pos < it.n) pf_sid = p.lst[it.L].idx[(int64_t)it.t * p.lst[it.L].row_stride + pos];
+      if (pos < it.n) pf_sid = LD(it.L).idx[(int64_t)it.t * LD(it.L).row_stride + pos];
     }
   };
   auto idx_finish = [&](const Item& it, int s) {
     if (w == 0) {
-      const ListDev& ld = p.lst[it.L];
+      const ListDev& ld = LD(it.L);
       const bool ok = !it.end && tid < KT && pf_sid >= 0 && pf_sid < ld.slots;
       uint64_t a = 0, sa = 0;
       if (ok) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   u32x4 stg_rp;
   auto rec_issue = [&](const Item& it, int s) {
     if (it.end || !sm.slot_any[s]) return;
-    const ListDev& ld = p.lst[it.L];
+    const ListDev& ld = LD(it.L);
     const uint64_t dummy = (uint64_t)ld.base;
     if (ld.format == SDA_NVFP4_288) {
 #pragma unroll
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const bool live = !it.end && sm.slot_any[s];
     if (tid == 0) sm.tile_any = live ? 1 : 0;
     if (!live) return;
-    const ListDev& ld = p.lst[it.L];
+    const ListDev& ld = LD(it.L);
     if (ld.format == SDA_NVFP4_288) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         for (int hb = 0; hb < NH2; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(kb[ks & 1] + rb * 16 * RS + 128 * (ks >> 1));
+          const bf16x8 a = *(const bf16x8*)(sm.tile + kb[ks & 1] + rb * 16 * RS + 128 * (ks >> 1));
 #pragma unroll
           for (int hb = 0; hb < NH2; ++hb)
             acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[hb][ks], acc[hb], 0, 0, 0);
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         }
         if constexpr (kRope) {
           if (w < 2) {
-            const bf16x8 a = *(const bf16x8*)(kr + rb * 16 * RS);
+            const bf16x8 a = *(const bf16x8*)(sm.tile + kr + rb * 16 * RS);
 #pragma unroll
             for (int hb = 0; hb < NH2; ++hb)
               acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrope[hb], acc[hb], 0, 0, 0);
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const char* v = vb[db & 3] + 128 * (db >> 2);
+        const char* v = sm.tile + vb[db & 3] + 128 * (db >> 2);
         const bf16x4 v0 = lds_read_tr16(v);
         const bf16x4 v1 = lds_read_tr16(v + 16 * RS);
         const bf16x8 B = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
