@@ -27,6 +27,7 @@
 
 #include "sda_device.h"
 #include "sda_internal.h"
+#include "sda_items.h"
 
 namespace sda {
 
@@ -45,55 +46,6 @@ struct DecodeSmem {
   uint64_t saddr[NSLOT][KT];   // where the row's scales come from (slot scale or the record's fp32 scales)
   int slot_any[NSLOT];
 };
-
-// A sub-tile of the part, as uniform scalars.
-struct Item {
-  int t, L, pos0, n, end;
-};
-
-// Walks the (token, tile, half) sequence of a part.
-struct ItemGen {
-  int t, i, j, n0, n1, tm, i_end, t_last, bt, bi, et, ei;
-  bool done;
-};
-
-__device__ __forceinline__ void gen_token(ItemGen& g, const DecodeParams& p, int t) {
-  g.t = t;
-  g.n0 = clamp_len(p.lst[0].lens, p.lst[0].width, t);
-  g.n1 = p.nlists > 1 ? clamp_len(p.lst[1].lens, p.lst[1].width, t) : 0;
-  g.tm = (g.n0 + kTileRows - 1) / kTileRows;
-  g.i = (t == g.bt) ? g.bi : 0;
-  g.j = 0;
-  g.i_end = (t == g.et) ? g.ei : token_tiles(g.n0, g.n1);
-}
-
-__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
-  Item it;
-  if (g.done) {
-    it.t = -1;
-    it.L = 0;
-    it.pos0 = 0;
-    it.n = 0;
-    it.end = 1;
-    return it;
-  }
-  it.t = g.t;
-  it.L = g.i < g.tm ? 0 : 1;
-  it.n = it.L == 0 ? g.n0 : g.n1;
-  it.pos0 = kTileRows * (it.L == 0 ? g.i : g.i - g.tm) + KT * g.j;
-  it.end = 0;
-  if (g.j == 0 && it.pos0 + KT < it.n) {
-    g.j = 1;
-  } else if (g.i + 1 < g.i_end) {
-    g.i += 1;
-    g.j = 0;
-  } else if (g.t + 1 <= g.t_last && g.t + 1 < p.T) {
-    gen_token(g, p, g.t + 1);
-  } else {
-    g.done = true;
-  }
-  return it;
-}
 
 template <int DQK, int NH2, int NTERM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH2 == 1 ? 3 : 1)))
@@ -265,17 +217,11 @@ void decode_kernel(DecodeParams p) {
 
   // ---- prologue: items k = 0..3, addresses of 0..2, records of 0 converted, records of 1 in flight
   ItemGen gen;
-  gen.bt = bt;
-  gen.bi = bi;
-  gen.et = et;
-  gen.ei = ei;
-  gen.t_last = (ei > 0) ? et : et - 1;
-  gen.done = false;
-  gen_token(gen, p, bt);
-  Item it0 = gen_next(gen, p);
-  Item it1 = gen_next(gen, p);
-  Item it2 = gen_next(gen, p);
-  Item it3 = gen_next(gen, p);
+  gen_init(gen, p, bt, bi, et, ei);
+  Item it0 = gen_next<KT>(gen, p);
+  Item it1 = gen_next<KT>(gen, p);
+  Item it2 = gen_next<KT>(gen, p);
+  Item it3 = gen_next<KT>(gen, p);
   idx_issue(it0);
   idx_finish(it0, 0);
   idx_issue(it1);
@@ -416,8 +362,8 @@ void decode_kernel(DecodeParams p) {
     // ---- epilogue after the token's last sub-tile in this part
     if (it1.end || it1.t != it0.t) {
       const int t = it0.t;
-      const int s_first = p.num_splits[t];
-      const int nsplit = p.num_splits[t + 1] - s_first;
+      const int s_first = it0.s_first;
+      const int nsplit = it0.nsplit;
       const int split_k = (t == bt) ? bk : 0;
 #pragma unroll
       for (int hb = 0; hb < NH2; ++hb) {
@@ -478,7 +424,7 @@ void decode_kernel(DecodeParams p) {
     it0 = it1;
     it1 = it2;
     it2 = it3;
-    it3 = gen_next(gen, p);
+    it3 = gen_next<KT>(gen, p);
     ++k;
     __syncthreads();  // the converted tile and the new addresses are visible
   }
@@ -494,8 +440,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int prec
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
-                         hipStream_t stream) {
+hipError_t launch_decode_tile(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
+                              hipStream_t stream) {
   if (d_qk == 576)
     return heads_per_group == 16 ? launch_decode_t<576, 1>(p, num_parts, precision, stream)
                                  : launch_decode_t<576, 2>(p, num_parts, precision, stream);
