@@ -29,7 +29,9 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
-               for f in ("sda_decode.hip", "sda_sched.hip", "sda_device.h", "sda_internal.h")]
+               for f in ("sda_decode.hip", "sda_decode_ring.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
+                         "sda_internal.h")]
+CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
 
 
 def log(*a):
@@ -80,6 +82,56 @@ def read_traffic(workload: str, sha: str):
         return None
 
 
+def _pmc_rows(path_dir):
+    """(kernel name, counter name, value) rows of every rocprofv3 counter-collection CSV under a dir."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(path_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""), float(r.get("Counter_Value", "nan"))))
+    return rows
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str):
+    """Turns the two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over a bench run with
+    --copy-calib into profiles/traffic_decode_<workload>.txt: the decode kernel's mean counters per
+    launch, each divided by what the same counter reads per byte of the calibration copy."""
+    w = wl.make_workload(workload, seed=0)
+    alg_bytes, _, _ = algorithmic_work(w)
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(d) if r[1] == name]
+        dec = [v for k, _, v in rows if "decode" in k and "kernel" in k]
+        cal = [v for k, _, v in rows if "elementwise" in k.lower() and "mul" in k.lower()]
+        if not dec or not cal:
+            raise SystemExit(f"no decode or calibration dispatches with {name} under {d}")
+        dec_names = sorted({k for k, _, _ in rows if "decode" in k and "kernel" in k})
+        out[name] = (sum(dec) / len(dec), sum(cal) / len(cal), len(dec), dec_names)
+    f_kib, f_cal, n_f, names = out["FETCH_SIZE"]
+    w_kib, w_cal, n_w, _ = out["WRITE_SIZE"]
+    f_factor = f_cal * 1024.0 / CALIB_BYTES
+    w_factor = w_cal * 1024.0 / CALIB_BYTES
+    hbm = f_kib * 1024.0 / f_factor + w_kib * 1024.0 / w_factor
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.txt")
+    with open(path, "w") as fh:
+        fh.write(f"# L2 <-> fabric traffic of the decode kernel, {workload}: rocprofv3 --pmc, one pass per counter\n")
+        fh.write(f"# command: {command}\n")
+        fh.write("# the calibration is an elementwise copy (x * 1) of 256 MiB in the same process\n")
+        fh.write(f"kernel = {' / '.join(n.split('(')[0] for n in names)}\n")
+        fh.write(f"kernel_sha = {kernel_sha()}\n")
+        fh.write(f"decode_dispatches = {n_f} / {n_w}\n")
+        fh.write(f"fetch_kib_per_launch = {f_kib:.1f}\n")
+        fh.write(f"write_kib_per_launch = {w_kib:.1f}\n")
+        fh.write(f"copy_fetch_factor = {f_factor:.4f}\n")
+        fh.write(f"copy_write_factor = {w_factor:.4f}\n")
+        fh.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        fh.write(f"alg_bytes_per_launch = {alg_bytes}\n")
+        fh.write(f"traffic_over_alg = {hbm / alg_bytes:.3f}\n")
+    print(open(path).read())
+
+
 def cpu_baseline(w, max_seconds: float = 20.0):
     import oracle
     threads = max(1, min(os.cpu_count() or 1, 16))
@@ -109,7 +161,16 @@ def main():
     ap.add_argument("--heads-per-group", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true", help="also time with rotating buffer sets larger than the MALL")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB elementwise copy (calibrates the counter-based traffic)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_decode_<workload>.txt from two rocprofv3 --pmc output dirs")
+    ap.add_argument("--pmc-command", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -250,6 +311,14 @@ def main():
         result["cold"] = {"ms_per_step": round(ms_cold, 5), "value": round(w.T / (ms_cold / 1e3), 1),
                           "buffer_sets": nsets}
         del sets
+
+    if args.copy_calib:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
