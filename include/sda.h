@@ -98,8 +98,12 @@ typedef struct sda_list {
  *  heads_per_group  query heads one workgroup computes; the grid is num_parts x H/heads_per_group
  *  fixed_overhead   scheduler cost of starting a token inside a part, in 64-row tiles
  *                   (DecodeImplMeta.fixed_overhead_num_blocks)
- *  precision        PV product precision: 3 = P split into three bf16 terms (fp32-accurate, the
- *                   default), 1 = P rounded once to bf16 (faster, ~2^-9 relative error per weight) */
+ *  precision        number of bf16 terms the softmax weights P are split into for the bf16 P.V
+ *                   product: 1 = P rounded once to bf16 (fastest; ~2^-9 relative error per weight,
+ *                   which can move bf16 outputs of magnitude >= 2 by one ulp, 2^-6, more often than
+ *                   the 1e-2 output tolerance allows), 2 = hi + lo terms (the default; ~2^-17), 3 =
+ *                   three terms whose sum is P exactly (fp32-accurate). Terms multiply the P.V
+ *                   matrix-core work. */
 typedef struct sda_plan {
   int32_t num_parts;
   int32_t heads_per_group;

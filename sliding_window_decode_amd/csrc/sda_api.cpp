@@ -89,7 +89,7 @@ int check_plan(const sda_plan* plan, int H) {
     return fail(SDA_ERR_UNSUPPORTED, "plan.heads_per_group must be 16 or 32 and divide H");
   if (plan->fixed_overhead < 0 || plan->fixed_overhead > 1024)
     return fail(SDA_ERR_INVALID_ARG, "plan.fixed_overhead out of range");
-  if (plan->precision != 1 && plan->precision != 3) return fail(SDA_ERR_INVALID_ARG, "plan.precision must be 1 or 3");
+  if (plan->precision < 1 || plan->precision > 3) return fail(SDA_ERR_INVALID_ARG, "plan.precision must be 1, 2 or 3");
   return SDA_OK;
 }
 
@@ -202,17 +202,19 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
   if (d_qk != 512 && d_qk != 576) return fail(SDA_ERR_UNSUPPORTED, "d_qk must be 512 or 576");
   if (num_cus <= 0) num_cus = 256;
-  // Heads per workgroup: 16 (two workgroups fit per CU); the other head groups of a part re-read the
-  // token's rows, mostly from L2 (a part's head groups land on the same XCD when num_parts % 8 == 0).
-  const int hb = 16;
+  // Heads per workgroup: 32 when H allows it (eight waves, one workgroup per CU, every record read once
+  // per 32 heads), else 16 (four waves, two workgroups per CU). The parts fill every workgroup slot
+  // once; a part's head groups land on the same XCD (shared L2) when num_parts % 8 == 0.
+  const int hb = H >= 32 ? 32 : 16;
   const int groups = H / hb;
-  int parts = (2 * num_cus) / groups;
+  const int slots_per_cu = (hb == 16 && d_qk == 512) ? 2 : 1;
+  int parts = (slots_per_cu * num_cus) / groups;
+  parts = ((parts + 7) / 8) * 8;
   if (parts < 8) parts = 8;
-  if (parts < 1) parts = 1;
   plan->num_parts = parts;
   plan->heads_per_group = hb;
   plan->fixed_overhead = 2;
-  plan->precision = 3;
+  plan->precision = 2;
   return SDA_OK;
 }
 

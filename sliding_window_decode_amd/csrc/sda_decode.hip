@@ -435,6 +435,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int prec
   dim3 grid(num_parts, p.H / (16 * NH2));
   if (precision == 1)
     hipLaunchKernelGGL((decode_kernel<DQK, NH2, 1>), grid, dim3(256), 0, stream, p);
+  else if (precision == 2)
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 2>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_kernel<DQK, NH2, 3>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -47,7 +47,7 @@ def test_format_tables_match_generators():
                                          (512, 16, 512, 128, 2048), (128, 128, 576, 2048, 0)])
 def test_make_plan_and_workspace(T, H, dqk, W, X):
     plan = sda.make_plan(T, H, dqk, W, X)
-    assert plan.num_parts >= 1 and H % plan.heads_per_group == 0 and plan.precision == 3
+    assert plan.num_parts >= 1 and H % plan.heads_per_group == 0 and plan.precision == 2
     ws = sda.workspace_bytes(T, H, 512, plan)
     assert ws >= (T + plan.num_parts) * H * 512 * 4 and ws % 256 == 0
 
@@ -118,7 +118,7 @@ def _call(q_shape=(4, 16, 512), fmt=sda.FP8_528, page_size=64, page_stride=None,
     (dict(extra=True, xfmt=sda.V32_656), sda.SDA_ERR_UNSUPPORTED),         # extra cache d_qk mismatch
     (dict(plan=sda.sda_plan(0, 16, 2, 3)), sda.SDA_ERR_INVALID_ARG),       # num_parts
     (dict(plan=sda.sda_plan(8, 24, 2, 3)), sda.SDA_ERR_UNSUPPORTED),       # heads per group
-    (dict(plan=sda.sda_plan(8, 16, 2, 2)), sda.SDA_ERR_INVALID_ARG),       # precision
+    (dict(plan=sda.sda_plan(8, 16, 2, 4)), sda.SDA_ERR_INVALID_ARG),       # precision
     (dict(ws_bytes=1024), sda.SDA_ERR_WORKSPACE),                          # workspace too small
     (dict(q_ptr=(1 << 20) + 2), sda.SDA_ERR_INVALID_ARG),                  # q misaligned
     (dict(meta=True), sda.SDA_ERR_INVALID_ARG),                            # meta without num_splits

@@ -213,14 +213,19 @@ def test_strided_q_and_out():
     assert torch.all(lbig[:, w.H:] == 7.0)
 
 
-def test_precision_one_term_on_many_rows():
-    """The faster single-term P mode on a top-k shape with many rows per token."""
-    w = wl.make_workload("c5_topk_v32", seed=4, T=2)
+@pytest.mark.parametrize("name,T", [("c5_topk_v32", 2), ("c3_swa_fp8extra", 8), ("c4_swa_nvfp4extra", 4),
+                                    ("c2_swa_h128", 4)])
+@pytest.mark.parametrize("precision", [1, 2, 3])
+def test_precision_modes(name, T, precision):
+    """Every P precision (one, two (the default) or three bf16 terms) on every kernel path; the single
+    term mode may flip more outputs of magnitude >= 2 by one bf16 ulp."""
+    w = wl.make_workload(name, seed=4, T=T)
     o_ref, l_ref = oracle.attention(w, nthreads=8)
-    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width)
-    plan.precision = 1
+    X = w.xlst.width if w.xlst is not None else 0
+    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
+    plan.precision = precision
     out, lse, _ = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what="precision 1")
+    compare(out, lse, o_ref, l_ref, what=f"{name} precision {precision}", count_flips=precision > 1)
 
 
 # ------------------------------------------------------------------ decode tables on the GPU
