@@ -130,10 +130,7 @@ sda::ListDev list_dev(const sda_cache* c, const sda_list* l) {
 namespace sda {
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream) {
-  bool fp4 = p.lst[0].format == SDA_NVFP4_288;
-  if (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288) fp4 = true;
-  return fp4 ? launch_decode_tile(p, num_parts, heads_per_group, d_qk, precision, stream)
-             : launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
+  return launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
 }
 }  // namespace sda
 

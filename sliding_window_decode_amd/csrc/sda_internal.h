@@ -1,5 +1,5 @@
 // sda_internal.h -- declarations shared by the host API (sda_api.cpp) and the HIP kernels
-// (sda_decode.hip, sda_decode_ring.hip, sda_sched.hip). Not part of the public ABI.
+// (sda_decode_ring.hip, sda_sched.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -94,11 +94,7 @@ __host__ __device__ inline int64_t part_quantum(int64_t total, int num_parts) {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_sched(const SchedParams& p, hipStream_t stream);
-// Decode kernels: the tile kernel (sda_decode.hip) takes every record format and stages the records
-// in registers; the ring kernel (sda_decode_ring.hip) takes the fp8 formats only and streams them into
-// LDS. launch_decode (sda_api.cpp) picks the ring kernel when no list is NVFP4.
-hipError_t launch_decode_tile(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
-                              hipStream_t stream);
+// The decode kernel (sda_decode_ring.hip); launch_decode (sda_api.cpp) forwards to it.
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
