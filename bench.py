@@ -29,7 +29,8 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
-               for f in ("sda_decode_ring.hip", "sda_items.h", "sda_sched.hip", "sda_device.h", "sda_internal.h")]
+               for f in ("sda_decode_ring.hip", "sda_decode_staged.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
+                         "sda_internal.h")]
 CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
 
 

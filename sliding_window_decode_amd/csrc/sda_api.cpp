@@ -130,7 +130,9 @@ sda::ListDev list_dev(const sda_cache* c, const sda_list* l) {
 namespace sda {
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream) {
-  return launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
+  const bool fp4 = p.lst[0].format == SDA_NVFP4_288 || (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288);
+  return fp4 ? launch_decode_staged(p, num_parts, heads_per_group, d_qk, precision, stream)
+             : launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
 }
 }  // namespace sda
 
@@ -200,11 +202,12 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   if (d_qk != 512 && d_qk != 576) return fail(SDA_ERR_UNSUPPORTED, "d_qk must be 512 or 576");
   if (num_cus <= 0) num_cus = 256;
   // Heads per workgroup: 32 when H allows it (eight waves, one workgroup per CU, every record read once
-  // per 32 heads), else 16 (four waves, two workgroups per CU). The parts fill every workgroup slot
-  // once; a part's head groups land on the same XCD (shared L2) when num_parts % 8 == 0.
+  // per 32 heads), else 16 (four waves; two workgroups per CU for fp8 records, three for NVFP4 ones:
+  // three parts per CU). The parts fill every workgroup slot once; a part's head groups land on the
+  // same XCD (shared L2) when num_parts % 8 == 0.
   const int hb = H >= 32 ? 32 : 16;
   const int groups = H / hb;
-  const int slots_per_cu = (hb == 16 && d_qk == 512) ? 2 : 1;
+  const int slots_per_cu = (hb == 16 && d_qk == 512) ? 3 : 1;
   int parts = (slots_per_cu * num_cus) / groups;
   parts = ((parts + 7) / 8) * 8;
   if (parts < 8) parts = 8;

@@ -30,8 +30,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "sda_device.h"
 #include "sda_internal.h"
 #include "sda_items.h"
@@ -40,100 +38,10 @@ namespace sda {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void gbl_void;
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
 // Masked rows gather from here: zero codes and zero scales, so they add nothing to P'V.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_record[1024];
 
-__device__ __forceinline__ void dma16(uint64_t src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(uint64_t src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 4, 0, 0);
-}
-
-// Workgroup barrier that does not wait for the gathers in flight (only for this wave's LDS
-// operations). The compiler's __syncthreads would also drain every global -> LDS load.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// ds_read_b64_tr_b8 (see lds_read_tr16 for the lane pattern; here 8 one-byte elements from lanes
-// 2e + i / 8). Issued as inline assembly: with the builtin the compiler drains every global -> LDS
-// load in flight before the read, as it cannot tell that the two touch different ring buffers. The
-// result may only be used after lds_wait().
-__device__ __forceinline__ i32x2 lds_tr8(uint32_t lds_addr) {
-  i32x2 r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(lds_addr));
-  return r;
-}
-// ds_read_b64_tr_b4: within each group of 16 lanes, lane i receives in nibble n the i-th nibble of the
-// 8 bytes read by lane n. Pointing lane n at row r0 + n, columns c0 .. c0 + 15 of a row-major e2m1
-// tile (two per byte, low nibble first) hands lane i column c0 + i of rows r0 .. r0 + 15.
-__device__ __forceinline__ i32x2 lds_tr4(uint32_t lds_addr) {
-  i32x2 r;
-  asm volatile("ds_read_b64_tr_b4 %0, %1" : "=v"(r) : "v"(lds_addr));
-  return r;
-}
-
-// The two e2m1 codes of byte SEL of w (low nibble first), each times its own scale, as a bf16 pair
-// (exact: a 2-bit times a 4-bit significand).
-template <int SEL>
-__device__ __forceinline__ uint32_t e2m1x2_scaled2_to_bf16(uint32_t w, float s0, float s1) {
-  f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-  const uint32_t a = __builtin_bit_cast(uint32_t, f[0] * s0);
-  const uint32_t b = __builtin_bit_cast(uint32_t, f[1] * s1);
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 e4m3 codes -> two bf16x8 (codes 0..7, 8..15), exact.
-__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 x, bf16x8& lo, bf16x8& hi) {
-  uint32_t y[8];
-  e4m3x4_to_bf16(x[0], y[0], y[1]);
-  e4m3x4_to_bf16(x[1], y[2], y[3]);
-  e4m3x4_to_bf16(x[2], y[4], y[5]);
-  e4m3x4_to_bf16(x[3], y[6], y[7]);
-  lo = __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
-  hi = __builtin_bit_cast(bf16x8, u32x4{y[4], y[5], y[6], y[7]});
-}
-
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(const i32x2 x) {
-  uint32_t y[4];
-  e4m3x4_to_bf16((uint32_t)x[0], y[0], y[1]);
-  e4m3x4_to_bf16((uint32_t)x[1], y[2], y[3]);
-  return __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
-}
-
 }  // namespace
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Waits until at most n' global operations of this wave are pending, n' the largest step <= n
-// (n is wave-uniform).
-__device__ __forceinline__ void vm_wait_atmost(int n) {
-  if (n >= 32) {
-    if (n >= 48) {
-      if (n >= 56) vm_wait<56>(); else vm_wait<48>();
-    } else {
-      if (n >= 40) vm_wait<40>(); else vm_wait<32>();
-    }
-  } else if (n >= 16) {
-    if (n >= 24) vm_wait<24>(); else vm_wait<16>();
-  } else if (n >= 8) {
-    if (n >= 12) vm_wait<12>(); else vm_wait<8>();
-  } else if (n >= 4) {
-    vm_wait<4>();
-  } else {
-    vm_wait<0>();
-  }
-}
 
 template <int DQK, int HS, int NB>
 struct RingSmem {
@@ -148,9 +56,8 @@ struct RingSmem {
 
 // HS head sets of 16 heads per workgroup (4 HS waves), NB ring buffers (tiles k+1 .. k+NB-1 in flight
 // while tile k is computed), NTERM bf16 terms of P'.
-template <int DQK, int HS, int NTERM, int NB, bool FP4>
-__global__ __launch_bounds__(256 * HS)
-__attribute__((amdgpu_waves_per_eu(HS == 2 || (DQK == 512 && NB == 2 && !FP4) ? 2 : 1)))
+template <int DQK, int HS, int NTERM, int NB>
+__global__ __launch_bounds__(256 * HS) __attribute__((amdgpu_waves_per_eu(HS == 2 || (DQK == 512 && NB == 2) ? 2 : 1)))
 void decode_ring_kernel(DecodeParams p) {
   using Smem = RingSmem<DQK, HS, NB>;
   constexpr int RS = Smem::RS;
@@ -158,11 +65,6 @@ void decode_ring_kernel(DecodeParams p) {
   constexpr int RW = 16 / HS;                 // rows gathered by each wave
   constexpr int NI = (RW * RSC + 63) / 64;    // gather instructions per wave and tile
   constexpr bool kRope = DQK == 576;
-  static_assert(!FP4 || DQK == 512, "NVFP4 records hold 512 dims");
-  constexpr bool kFp4 = FP4;                  // NVFP4 tiles possible
-  constexpr int kRsFp4 = 304;                 // ring row stride of an NVFP4 tile (19 chunks)
-  constexpr int NI4 = (RW * (kRsFp4 / 16) + 63) / 64;
-  constexpr int kScaleTab = kTileRows * kRsFp4;  // NVFP4: per-(16-dim block, row) fp32 scales, after the rows
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -204,38 +106,24 @@ void decode_ring_kernel(DecodeParams p) {
     }
     const uint32_t vm = (uint32_t)__ballot(ok) & ((1u << RW) - 1u);
     if (lane < RW) sm.raddr[w][lane] = ra;  // read back by the same wave only
-    const int nch = ld.rec >> 4;  // chunks in a record (18, 32, 33 or 41)
-    // one code path per ring row stride (R chunks; NVFP4 tiles use 19, the others RSC)
-    auto issue = [&](auto r_c) {
-      constexpr int R = decltype(r_c)::value;
-      constexpr int N = (RW * R + 63) / 64;
-      char* dst = sm.ring[b] + RW * w * R * 16;
-      // all source addresses first: the compiler keeps LDS reads behind earlier global -> LDS loads.
-      // The spare ring chunk of a 288- or 512-byte record takes a copy of its chunk 0 (never read);
-      // no branch, so that the address reads are not serialized.
-      uint64_t src[N];
+    const int nch = ld.rec >> 4;  // chunks in a record (32, 33 or 41)
+    char* dst = sm.ring[b] + RW * w * RS;
+    // all source addresses first: the compiler keeps LDS reads behind earlier global -> LDS loads.
+    // The spare ring chunk of a 512-byte record takes a copy of its chunk 0 (never read); no branch,
+    // so that the address reads are not serialized.
+    uint64_t src[NI];
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int c = 64 * i + lane;
-        const int rl = c / R, ch = c - rl * R;
-        src[i] = sm.raddr[w][rl % RW] + 16 * (ch < nch ? ch : 0);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int c = 64 * i + lane;
+      const int rl = c / RSC, ch = c - rl * RSC;
+      src[i] = sm.raddr[w][rl % RW] + 16 * (ch < nch ? ch : 0);
+    }
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        if (i < N - 1 || 64 * i + lane < RW * R) dma16(src[i], dst + 1024 * i);
-      }
-    };
-    if (kFp4 && ld.format == SDA_NVFP4_288)
-      issue(std::integral_constant<int, kRsFp4 / 16>{});
-    else
-      issue(std::integral_constant<int, RSC>{});
+    for (int i = 0; i < NI; ++i) {
+      if (i < NI - 1 || 64 * i + lane < RW * RSC) dma16(src[i], dst + 1024 * i);
+    }
     if (ld.format == SDA_FP8_SLOTSCALE && lane < RW) dma4(sa, &sm.sscale[b][RW * w]);
     return vm;
-  };
-  // global -> LDS loads one gather issues (the slot-scale load not counted)
-  auto gather_ops = [&](const Item& it) -> int {
-    if (it.end) return 0;
-    return (kFp4 && LD(it.L).format == SDA_NVFP4_288) ? NI4 : NI;
   };
 
   // ---- prologue: items k = 0 .. NB, gathers of tiles 0 .. NB-2 in flight, slot ids of tile NB-1
@@ -353,7 +241,7 @@ void decode_ring_kernel(DecodeParams p) {
     cnt_iter[r] = 0;
     cnt_tail[r] = QN;
 #pragma unroll
-    for (int i2 = r + 1; i2 + 1 < NB; ++i2) cnt_tail[r] += gather_ops(its[i2]);
+    for (int i2 = r + 1; i2 + 1 < NB; ++i2) cnt_tail[r] += its[i2].end ? 0 : NI;
   }
 
   int k = 0;
@@ -383,32 +271,19 @@ void decode_ring_kernel(DecodeParams p) {
       const int bg = (k + NB - 1) % NB;
       const uint32_t vm = gather(its[NB - 1], sid_next, bg);
       if (lane == 0) sm.vmask[bg][w] = vm;
-      c_iter += gather_ops(its[NB - 1]);
+      c_iter += NI;
     }
     sid_next = sid_new;
 
     const Item it0 = its[0], it1 = its[1];
     const ListDev& ld = LD(it0.L);
     const bool slot_scaled = ld.format == SDA_FP8_SLOTSCALE;
-    const bool fp4 = kFp4 && ld.format == SDA_NVFP4_288;
     const uint32_t vmw = HS == 1 ? sm.vmask[b][wr] : (sm.vmask[b][2 * wr] | (sm.vmask[b][2 * wr + 1] << 8));
     uint32_t vany = 0;
 #pragma unroll
     for (int j = 0; j < 4 * HS; ++j) vany |= sm.vmask[b][j];
     const bool any = vany != 0;
     const char* ring = sm.ring[b];
-
-    if (any && fp4) {
-      // NVFP4: the per-(16-dim block, row) scales as an fp32 table [block][row] in the spare space of
-      // the ring buffer, for PV (read after the next barrier)
-      float* tab = (float*)(sm.ring[b] + kScaleTab);
-#pragma unroll
-      for (int q = tid >> 6; q < 8; q += 4 * HS) {
-        const uint32_t x = *(const uint32_t*)(ring + lane * kRsFp4 + 256 + 4 * q);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tab[(4 * q + c) * 64 + lane] = e4m3_to_f32((x >> (8 * c)) & 0xFFu);
-      }
-    }
 
     if (any) {
       // ---- QK^T for rows 16wr .. 16wr+15
@@ -419,25 +294,10 @@ void decode_ring_kernel(DecodeParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         bf16x8 lo[4], hi[4];
-        if (!fp4) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 x = *(const u32x4*)(ring + qk_off + 64 * (2 * g + half));
-            e4m3x16_to_bf16(x, lo[g], hi[g]);
-          }
-        } else {
-          // dims 64j + 16G .. + 15 (j = 2g + half): bytes 32j + 8G .. + 7, block 4j + G
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j = 2 * g + half;
-            const i32x2 x = *(const i32x2*)(ring + (16 * wr + li) * kRsFp4 + 32 * j + 8 * G);
-            const float sc = e4m3_to_f32(*(const uint8_t*)(ring + (16 * wr + li) * kRsFp4 + 256 + 4 * j + G));
-            const uint32_t w0 = (uint32_t)x[0], w1 = (uint32_t)x[1];
-            lo[g] = __builtin_bit_cast(bf16x8, u32x4{e2m1x2_scaled_to_bf16<0>(w0, sc), e2m1x2_scaled_to_bf16<1>(w0, sc),
-                                                     e2m1x2_scaled_to_bf16<2>(w0, sc), e2m1x2_scaled_to_bf16<3>(w0, sc)});
-            hi[g] = __builtin_bit_cast(bf16x8, u32x4{e2m1x2_scaled_to_bf16<0>(w1, sc), e2m1x2_scaled_to_bf16<1>(w1, sc),
-                                                     e2m1x2_scaled_to_bf16<2>(w1, sc), e2m1x2_scaled_to_bf16<3>(w1, sc)});
-          }
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 x = *(const u32x4*)(ring + qk_off + 64 * (2 * g + half));
+          e4m3x16_to_bf16(x, lo[g], hi[g]);
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -454,10 +314,7 @@ void decode_ring_kernel(DecodeParams p) {
       }
       // fold the rows' scales, mask, write the scores
       f32x4 sc[4];
-      if (fp4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = f32x4{1.f, 1.f, 1.f, 1.f};
-      } else if (slot_scaled) {
+      if (slot_scaled) {
         const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * wr + 4 * G];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
@@ -475,7 +332,7 @@ void decode_ring_kernel(DecodeParams p) {
       }
       sm.sx[hs][wr][lane] = s;
       // the scale of dim group wr for every row (PV of both head sets)
-      if (hs == 0 && !slot_scaled && !fp4) sm.vs[wr][lane] = *(const float*)(ring + vs_off);
+      if (hs == 0 && !slot_scaled) sm.vs[wr][lane] = *(const float*)(ring + vs_off);
     }
     barrier_lds();  // scores of all rows visible
 
@@ -487,17 +344,15 @@ void decode_ring_kernel(DecodeParams p) {
     }
 
     if (any) {
-      // ---- online softmax; lane (head li, G) holds rows 32 kk + 8 G + e, e = 0..7 (the k-steps of
-      // the fp8 PV operand), or 16 G + 8 kk + e for NVFP4 tiles (those of the tr4 operand)
+      // ---- online softmax; lane (head li, G) holds rows 32 kk + 8 G + e, e = 0..7
       float pv[2][8];
       {
         float z[2][8];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const int wv = fp4 ? G : 2 * kk + (G >> 1);
-          const int d0 = fp4 ? 2 * kk : 2 * (G & 1);
-          const f32x4 a = sm.sx[hs][wv][16 * d0 + li];
-          const f32x4 c = sm.sx[hs][wv][16 * (d0 + 1) + li];
+          const int wv = 2 * kk + (G >> 1);
+          const f32x4 a = sm.sx[hs][wv][16 * (2 * (G & 1)) + li];
+          const f32x4 c = sm.sx[hs][wv][16 * (2 * (G & 1) + 1) + li];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             z[kk][r] = a[r];
@@ -543,11 +398,8 @@ void decode_ring_kernel(DecodeParams p) {
         const float* vsrc = slot_scaled ? sm.sscale[b] : sm.vs[wr];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          f32x4 a = f32x4{1.f, 1.f, 1.f, 1.f}, c = a;  // NVFP4: the scales are applied to V
-          if (!fp4) {
-            a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
-            c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
-          }
+          const f32x4 a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
+          const f32x4 c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
           float pg[8];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -586,49 +438,16 @@ void decode_ring_kernel(DecodeParams p) {
           }
         }
       };
-      if (!fp4) {
-        read_half(0);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(x[0][0][0]), "+v"(x[0][0][1]), "+v"(x[0][1][0]), "+v"(x[0][1][1]), "+v"(x[0][2][0]),
-                       "+v"(x[0][2][1]), "+v"(x[0][3][0]), "+v"(x[0][3][1]));
-        read_half(1);
-        mma_half(0);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(x[1][0][0]), "+v"(x[1][0][1]), "+v"(x[1][1][0]), "+v"(x[1][1][1]), "+v"(x[1][2][0]),
-                       "+v"(x[1][2][1]), "+v"(x[1][3][0]), "+v"(x[1][3][1]));
-        mma_half(1);
-      } else if constexpr (kFp4) {
-        // NVFP4: lane (column li, G) of dim block db gets rows 16G .. 16G+15 of dim 128wr + 16db + li
-        // (one tr4 read), times each row's scale of that block, as the two k-steps' operands
-        const uint32_t v4addr = lds_u32(ring) + (uint32_t)((16 * G + li) * kRsFp4 + 64 * wr);
-        const float* tab = (const float*)(sm.ring[b] + kScaleTab) + 16 * G;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-        i32x2 y[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) y[d] = lds_tr4(v4addr + 8 * (4 * half + d));
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int db = 4 * half + d;
-          const float* ts = tab + (8 * wr + db) * 64;
-          const f32x4 s0 = *(const f32x4*)(ts), s1 = *(const f32x4*)(ts + 4);
-          const f32x4 s2 = *(const f32x4*)(ts + 8), s3 = *(const f32x4*)(ts + 12);
-          const uint32_t w0 = (uint32_t)y[d][0], w1 = (uint32_t)y[d][1];
-          const bf16x8 B0 = __builtin_bit_cast(
-              bf16x8, u32x4{e2m1x2_scaled2_to_bf16<0>(w0, s0[0], s0[1]), e2m1x2_scaled2_to_bf16<1>(w0, s0[2], s0[3]),
-                            e2m1x2_scaled2_to_bf16<2>(w0, s1[0], s1[1]), e2m1x2_scaled2_to_bf16<3>(w0, s1[2], s1[3])});
-          const bf16x8 B1 = __builtin_bit_cast(
-              bf16x8, u32x4{e2m1x2_scaled2_to_bf16<0>(w1, s2[0], s2[1]), e2m1x2_scaled2_to_bf16<1>(w1, s2[2], s2[3]),
-                            e2m1x2_scaled2_to_bf16<2>(w1, s3[0], s3[1]), e2m1x2_scaled2_to_bf16<3>(w1, s3[2], s3[3])});
-#pragma unroll
-          for (int t = 0; t < NTERM; ++t) {
-            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][t], B0, O[db], 0, 0, 0);
-            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][t], B1, O[db], 0, 0, 0);
-          }
-        }
-        }
-      }
+      read_half(0);
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(x[0][0][0]), "+v"(x[0][0][1]), "+v"(x[0][1][0]), "+v"(x[0][1][1]), "+v"(x[0][2][0]),
+                     "+v"(x[0][2][1]), "+v"(x[0][3][0]), "+v"(x[0][3][1]));
+      read_half(1);
+      mma_half(0);
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(x[1][0][0]), "+v"(x[1][0][1]), "+v"(x[1][1][0]), "+v"(x[1][1][1]), "+v"(x[1][2][0]),
+                     "+v"(x[1][2][1]), "+v"(x[1][3][0]), "+v"(x[1][3][1]));
+      mma_half(1);
     }
 
     if (it1.end || it1.t != it0.t) {
@@ -652,34 +471,27 @@ void decode_ring_kernel(DecodeParams p) {
   if (ep_t >= 0) epilogue(ep_t, ep_s, ep_n);
 }
 
-template <int DQK, int HS, int NB, bool FP4>
+template <int DQK, int HS, int NB>
 static hipError_t launch_ring_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * HS));
   if (precision == 1)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB, FP4>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB>), grid, dim3(256 * HS), 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB, FP4>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB>), grid, dim3(256 * HS), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB, FP4>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB>), grid, dim3(256 * HS), 0, stream, p);
   return hipGetLastError();
 }
 
-// fp8 lists only: 16 heads per workgroup -> two workgroups per CU with two ring buffers each (one with
-// three for 576-dim records); 32 heads (eight waves, one workgroup per CU) -> three ring buffers.
-// A list of NVFP4 records (512 dims): the kernel with the NVFP4 paths; 16 heads -> one workgroup per
-// CU (every register of a SIMD for its one wave) with four ring buffers.
+// 16 heads per workgroup: two workgroups per CU, two ring buffers each. 32 heads per workgroup (eight
+// waves, one workgroup per CU): three ring buffers.
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream) {
-  bool fp4 = p.lst[0].format == SDA_NVFP4_288;
-  if (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288) fp4 = true;
   if (d_qk == 576)
-    return heads_per_group == 16 ? launch_ring_t<576, 1, 2, false>(p, num_parts, precision, stream)
-                                 : launch_ring_t<576, 2, 3, false>(p, num_parts, precision, stream);
-  if (fp4)
-    return heads_per_group == 16 ? launch_ring_t<512, 1, 4, true>(p, num_parts, precision, stream)
-                                 : launch_ring_t<512, 2, 3, true>(p, num_parts, precision, stream);
-  return heads_per_group == 16 ? launch_ring_t<512, 1, 2, false>(p, num_parts, precision, stream)
-                               : launch_ring_t<512, 2, 3, false>(p, num_parts, precision, stream);
+    return heads_per_group == 16 ? launch_ring_t<576, 1, 2>(p, num_parts, precision, stream)
+                                 : launch_ring_t<576, 2, 3>(p, num_parts, precision, stream);
+  return heads_per_group == 16 ? launch_ring_t<512, 1, 2>(p, num_parts, precision, stream)
+                               : launch_ring_t<512, 2, 3>(p, num_parts, precision, stream);
 }
 
 }  // namespace sda

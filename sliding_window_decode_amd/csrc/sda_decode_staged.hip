@@ -1,0 +1,455 @@
+// sda_decode_staged.hip -- split-KV decode attention for calls with an NVFP4 list, on gfx950: records
+// staged through registers, widened into a bf16 tile in LDS.
+//
+// Workgroup = one scheduler part x a group of 16 or 32 query heads, 4 waves. Wave w owns output dims
+// [128w, 128w + 128) of every head of the group (its O accumulator: 16-32 heads x 128 dims, fp32).
+// A part is a run of (token, 64-position tile) items; each tile is processed as two 32-row sub-tiles.
+//
+// Pipeline per workgroup, sub-tile k:
+//   slot ids of sub-tile k+3 are loaded while sub-tile k computes (they become record addresses at
+//   the end of the iteration); the records of sub-tile k+1 are already in flight in registers (issued
+//   one iteration earlier, branch-free: masked rows read a dummy address and are zeroed later).
+//   compute(k): QK^T partial over the wave's 128 dims (one dequant scale group) with
+//               v_mfma_f32_16x16x32_bf16, KV rows on M, heads on N; partial x that group's scale ->
+//               LDS; sum of the four partials; online softmax in base 2 (the reference max moves only
+//               when a tile exceeds it by more than 8); O += P' V with P' = p x scale split into NTERM
+//               bf16 terms and V read transposed from the tile with ds_read_b64_tr_b16
+//   convert(k+1): the staged records -> exact bf16 codes in the row-major LDS tile (16-byte chunks
+//               XOR-swizzled), fp32 scales -> a 32 x 4 LDS table; then the records of k+2 are issued.
+// After a token's last sub-tile in the part: the final bf16 output and LSE (sink folded in) when the
+// part holds the whole token, otherwise a normalized fp32 partial and its LSE for the combine kernel.
+// Sources: masked softmax attention (native_swa_decode.py, _fallback_batched_sdp); gather, validity
+// and page addressing (vLLM swapab_decode_attn, stage_inputs); online softmax (native_swa_decode.py,
+// BlackwellSWADecodeKernel); swap-AB score product and the sink merge (vLLM swapab_decode_attn,
+// device kernel steps 3 and 9); split buffers (FlashMLA sparse_decode.h, o_accum / lse_accum).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sda_device.h"
+#include "sda_internal.h"
+#include "sda_items.h"
+
+namespace sda {
+
+constexpr int KT = 32;    // rows per sub-tile
+constexpr int NSLOT = 3;  // address slots: sub-tiles k+1, k+2, k+3
+
+template <int DQK, int NH2>
+struct DecodeSmem {
+  static constexpr int RS = DQK * 2;  // bytes per bf16 row
+  char tile[KT * RS];
+  f32x4 spart[4][2][NH2][64];  // QK partials [wave][row block][head block][lane]
+  float scale[KT][4];          // the four 128-dim scales of each row of the tile (0 = masked row)
+  int valid[KT];
+  int tile_any;
+  uint64_t addr[NSLOT][KT];    // record address per row, 0 = masked
+  uint64_t saddr[NSLOT][KT];   // where the row's scales come from (slot scale or the record's fp32 scales)
+  int slot_any[NSLOT];
+};
+
+template <int DQK, int NH2, int NTERM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH2 == 1 ? 3 : 1)))
+void decode_kernel(DecodeParams p) {
+  constexpr int RS = DecodeSmem<DQK, NH2>::RS;
+  constexpr bool kRope = DQK == 576;
+  __shared__ DecodeSmem<DQK, NH2> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int G = lane >> 4, li = lane & 15;
+  const int h0 = blockIdx.y * (16 * NH2);
+
+  const ListDev lst0 = p.lst[0];
+  const ListDev lst1 = p.lst[p.nlists > 1 ? 1 : 0];
+  auto LD = [&](int L) -> const ListDev& { return L ? lst1 : lst0; };
+  const int32_t* mt = p.meta + (int64_t)blockIdx.x * SDA_META_INTS;
+  const int bt = mt[0], bi = mt[1], et = mt[2], ei = mt[3], bk = mt[4];
+  if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
+
+  // ---- per-lane LDS bases (rows of a sub-tile start at multiples of 8, so a lane's swizzle term is
+  // the same for every row it touches; every access below is base + a compile-time offset)
+  uint32_t kb[2], kr, vb[4];  // byte offsets into sm.tile
+  {
+    const int f = ((li & 3) << 1) | ((li >> 2) & 1);  // K operand rows li (+16 rb)
+    kb[0] = li * RS + 256 * w + 16 * (G ^ f);
+    kb[1] = li * RS + 256 * w + 16 * ((4 + G) ^ f);
+    kr = li * RS + 16 * (64 + ((4 * (w & 1) + G) ^ f));
+    const int rv = 4 * G + (li >> 2);  // V operand rows rv .. rv + 3 (+16)
+    const int fv = ((rv & 3) << 1) | ((rv >> 2) & 1);
+    const int cb = (li & 3) >> 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vb[q] = rv * RS + 256 * w + 16 * ((2 * q + cb) ^ fv) + 8 * (li & 1);
+  }
+
+  // ---- slot ids -> addresses (threads 0..31, one row each)
+  int pf_sid = -1;
+  auto idx_issue = [&](const Item& it) {
+    pf_sid = -1;
+    if (!it.end && tid < KT) {
+      const int pos = it.pos0 + tid;
+      if (pos < it.n) pf_sid = LD(it.L).idx[(int64_t)it.t * LD(it.L).row_stride + pos];
+    }
+  };
+  auto idx_finish = [&](const Item& it, int s) {
+    if (w == 0) {
+      const ListDev& ld = LD(it.L);
+      const bool ok = !it.end && tid < KT && pf_sid >= 0 && pf_sid < ld.slots;
+      uint64_t a = 0, sa = 0;
+      if (ok) {
+        const uint32_t pg = (uint32_t)pf_sid >> ld.page_shift;
+        const uint32_t off = (uint32_t)pf_sid & ((1u << ld.page_shift) - 1u);
+        a = (uint64_t)ld.base + (uint64_t)pg * (uint64_t)ld.page_stride + (uint64_t)off * (uint64_t)ld.rec;
+        sa = ld.format == SDA_FP8_SLOTSCALE ? (uint64_t)(ld.slot_scale + pf_sid) : a + 512;
+      }
+      if (tid < KT) {
+        sm.addr[s][tid] = a;
+        sm.saddr[s][tid] = sa;
+      }
+      const uint64_t any = __ballot(ok);
+      if (tid == 0) sm.slot_any[s] = any != 0 ? 1 : 0;
+    }
+  };
+
+  // ---- record staging (registers): the sub-tile's data chunks, its scale chunk and rope chunk
+  u32x4 stg[4];
+  uint32_t stg_sb[2];
+  u32x4 stg_sc;
+  u32x4 stg_rp;
+  auto rec_issue = [&](const Item& it, int s) {
+    if (it.end || !sm.slot_any[s]) return;
+    const ListDev& ld = LD(it.L);
+    const uint64_t dummy = (uint64_t)ld.base;
+    if (ld.format == SDA_NVFP4_288) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = (tid >> 4) + 16 * k, c = tid & 15;
+        const uint64_t a = sm.addr[s][r];
+        stg[k] = ld_global_16(a ? a + 16 * c : dummy);
+        stg_sb[k] = ld_global_u16(a ? a + 256 + 2 * c : dummy);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = (tid >> 5) + 8 * k, c = tid & 31;
+        const uint64_t a = sm.addr[s][r];
+        stg[k] = ld_global_16(a ? a + 16 * c : dummy);
+      }
+      if (tid < KT) {
+        const uint64_t sa = sm.saddr[s][tid];
+        if (ld.format == SDA_FP8_SLOTSCALE)
+          stg_sc[0] = *(gbl_u32*)(sa ? sa : dummy);
+        else
+          stg_sc = ld_global_16(sa ? sa : dummy);
+      }
+      if constexpr (kRope) {
+        const uint64_t a = sm.addr[s][tid >> 3];
+        stg_rp = ld_global_16(a ? a + 528 + 16 * (tid & 7) : dummy);
+      }
+    }
+  };
+  auto rec_convert = [&](const Item& it, int s) {
+    const bool live = !it.end && sm.slot_any[s];
+    if (tid == 0) sm.tile_any = live ? 1 : 0;
+    if (!live) return;
+    const ListDev& ld = LD(it.L);
+    if (ld.format == SDA_NVFP4_288) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = (tid >> 4) + 16 * k, c = tid & 15;
+        const bool ok = sm.addr[s][r] != 0;
+        const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
+        const float s0 = e4m3_to_f32(stg_sb[k] & 0xFFu), s1 = e4m3_to_f32((stg_sb[k] >> 8) & 0xFFu);
+        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        char* row = sm.tile + r * RS;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sc = q < 2 ? s0 : s1;
+          u32x4 o;
+          o[0] = e2m1x2_scaled_to_bf16<0>(x[q], sc);
+          o[1] = e2m1x2_scaled_to_bf16<1>(x[q], sc);
+          o[2] = e2m1x2_scaled_to_bf16<2>(x[q], sc);
+          o[3] = e2m1x2_scaled_to_bf16<3>(x[q], sc);
+          const int cc = 4 * c + q;
+          *(u32x4*)(row + 16 * ((cc & ~7) | ((cc ^ f) & 7))) = o;
+        }
+      }
+      if (tid < KT) {
+        const float v = sm.addr[s][tid] != 0 ? 1.0f : 0.0f;
+        *(f32x4*)sm.scale[tid] = f32x4{v, v, v, v};
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = (tid >> 5) + 8 * k, c = tid & 31;
+        const bool ok = sm.addr[s][r] != 0;
+        const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
+        uint32_t y[8];
+        e4m3x4_to_bf16(x[0], y[0], y[1]);
+        e4m3x4_to_bf16(x[1], y[2], y[3]);
+        e4m3x4_to_bf16(x[2], y[4], y[5]);
+        e4m3x4_to_bf16(x[3], y[6], y[7]);
+        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        char* row = sm.tile + r * RS;
+        const int c0 = 2 * c, c1 = 2 * c + 1;
+        *(u32x4*)(row + 16 * ((c0 & ~7) | ((c0 ^ f) & 7))) = u32x4{y[0], y[1], y[2], y[3]};
+        *(u32x4*)(row + 16 * ((c1 & ~7) | ((c1 ^ f) & 7))) = u32x4{y[4], y[5], y[6], y[7]};
+      }
+      if (tid < KT) {
+        const bool ok = sm.addr[s][tid] != 0;
+        f32x4 sc;
+        if (ld.format == SDA_FP8_SLOTSCALE) {
+          const float v = __builtin_bit_cast(float, stg_sc[0]);
+          sc = f32x4{v, v, v, v};
+        } else {
+          sc = __builtin_bit_cast(f32x4, stg_sc);
+        }
+        *(f32x4*)sm.scale[tid] = ok ? sc : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if constexpr (kRope) {
+        const int r = tid >> 3, c = 64 + (tid & 7);
+        const bool ok = sm.addr[s][r] != 0;
+        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        *(u32x4*)(sm.tile + r * RS + 16 * ((c & ~7) | ((c ^ f) & 7))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < KT) sm.valid[tid] = sm.addr[s][tid] != 0 ? 1 : 0;
+  };
+
+  // ---- prologue: items k = 0..3, addresses of 0..2, records of 0 converted, records of 1 in flight
+  ItemGen gen;
+  gen_init(gen, p, bt, bi, et, ei);
+  Item it0 = gen_next<KT>(gen, p);
+  Item it1 = gen_next<KT>(gen, p);
+  Item it2 = gen_next<KT>(gen, p);
+  Item it3 = gen_next<KT>(gen, p);
+  idx_issue(it0);
+  idx_finish(it0, 0);
+  idx_issue(it1);
+  idx_finish(it1, 1);
+  idx_issue(it2);
+  idx_finish(it2, 2);
+  __syncthreads();
+  rec_issue(it0, 0);
+  rec_convert(it0, 0);
+  rec_issue(it1, 1);
+  __syncthreads();
+
+  bf16x8 qreg[NH2][4];
+  bf16x8 qrope[NH2];
+  f32x4 O[NH2][8];
+  float m[NH2], l[NH2];
+  bool token_start = true;
+  int k = 0;
+
+  while (true) {
+    if (token_start) {
+      const uint16_t* qp = p.q + (int64_t)it0.t * p.q_st + 128 * w + 8 * G;
+#pragma unroll
+      for (int hb = 0; hb < NH2; ++hb) {
+        const uint16_t* qh = qp + (int64_t)(h0 + 16 * hb + li) * p.q_sh;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
+        if constexpr (kRope) qrope[hb] = *(const bf16x8*)(qh - 128 * w + 512 + 32 * (w & 1));
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[hb] = kNegInf;
+        l[hb] = 0.f;
+      }
+      token_start = false;
+    }
+    idx_issue(it3);  // in flight during this sub-tile's compute
+
+    if (sm.tile_any) {
+      // ---- QK^T partial over this wave's 128 dims
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 acc[NH2];
+#pragma unroll
+        for (int hb = 0; hb < NH2; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(sm.tile + kb[ks & 1] + rb * 16 * RS + 128 * (ks >> 1));
+#pragma unroll
+          for (int hb = 0; hb < NH2; ++hb)
+            acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[hb][ks], acc[hb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float s = sm.scale[rb * 16 + 4 * G + r][w];
+#pragma unroll
+          for (int hb = 0; hb < NH2; ++hb) acc[hb][r] *= s;
+        }
+        if constexpr (kRope) {
+          if (w < 2) {
+            const bf16x8 a = *(const bf16x8*)(sm.tile + kr + rb * 16 * RS);
+#pragma unroll
+            for (int hb = 0; hb < NH2; ++hb)
+              acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrope[hb], acc[hb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int hb = 0; hb < NH2; ++hb) sm.spart[w][rb][hb][lane] = acc[hb];
+      }
+      __syncthreads();
+
+      // ---- full scores and the online softmax (lane (head li of block hb, G) holds rows 16 rb + 4 G + r)
+      float pv[NH2][8];
+#pragma unroll
+      for (int hb = 0; hb < NH2; ++hb) {
+        float z[8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4 s = sm.spart[0][rb][hb][lane];
+#pragma unroll
+          for (int ww = 1; ww < 4; ++ww) s += sm.spart[ww][rb][hb][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[4 * rb + r] = sm.valid[rb * 16 + 4 * G + r] ? s[r] * p.scale_log2 : kNegInf;
+        }
+        float tmax = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
+        tmax = max_across_groups(tmax);
+        const bool bump = tmax > m[hb] + 8.0f;
+        const float m_new = bump ? tmax : m[hb];
+        const float alpha = bump ? fast_exp2(m[hb] - m_new) : 1.0f;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[hb][e] = (m_new == kNegInf) ? 0.f : fast_exp2(z[e] - m_new);
+          ps += pv[hb][e];
+        }
+        l[hb] = l[hb] * alpha + ps;
+        m[hb] = m_new;
+        if (__any(bump)) {
+          float ar[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * G + r);
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[hb][db][r] *= ar[r];
+          }
+        }
+      }
+
+      // ---- O += P' V over this wave's 128 dims
+      bf16x8 A[NH2][NTERM];
+#pragma unroll
+      for (int hb = 0; hb < NH2; ++hb) {
+        float pg[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = (e < 4) ? 4 * G + e : 16 + 4 * G + (e - 4);
+          pg[e] = pv[hb][e] * sm.scale[row][w];
+        }
+        split_terms<NTERM>(pg, A[hb]);
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const char* v = sm.tile + vb[db & 3] + 128 * (db >> 2);
+        const bf16x4 v0 = lds_read_tr16(v);
+        const bf16x4 v1 = lds_read_tr16(v + 16 * RS);
+        const bf16x8 B = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int hb = 0; hb < NH2; ++hb) {
+#pragma unroll
+          for (int t = 0; t < NTERM; ++t)
+            O[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[hb][t], B, O[hb][db], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- epilogue after the token's last sub-tile in this part
+    if (it1.end || it1.t != it0.t) {
+      const int t = it0.t;
+      const int s_first = it0.s_first;
+      const int nsplit = it0.nsplit;
+      const int split_k = (t == bt) ? bk : 0;
+#pragma unroll
+      for (int hb = 0; hb < NH2; ++hb) {
+        const float lt = sum_across_groups(l[hb]);
+        const int h = h0 + 16 * hb + li;
+        float inv, lse_out;
+        if (nsplit <= 1) {
+          const bool has_sink = p.sink != nullptr;
+          const float s2 = has_sink ? p.sink[h] * kLog2e : kNegInf;
+          const float Mx = fmaxf(m[hb], s2);
+          if (Mx == kNegInf) {
+            inv = 0.f;
+            lse_out = kNegInf;
+          } else if (s2 == kPosInf) {
+            inv = 0.f;
+            lse_out = kPosInf;
+          } else {
+            const float fo = (m[hb] == kNegInf) ? 0.f : fast_exp2(m[hb] - Mx);
+            const float den = lt * fo + (has_sink ? fast_exp2(s2 - Mx) : 0.f);
+            inv = den > 0.f ? fo / den : 0.f;
+            lse_out = den > 0.f ? (Mx + __log2f(den)) * kLn2 : kNegInf;
+          }
+        } else {
+          inv = lt > 0.f ? 1.0f / lt : 0.f;
+          lse_out = lt > 0.f ? (m[hb] + __log2f(lt)) * kLn2 : kNegInf;
+        }
+        float ir[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * G + r);
+        if (nsplit <= 1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)(h0 + 16 * hb + 4 * G + r) * p.o_sh + 128 * w + li;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) orow[16 * db] = f32_to_bf16_bits(O[hb][db][r] * ir[r]);
+          }
+          if (w == 0 && G == 0) p.lse[(int64_t)t * p.l_st + h] = lse_out;
+        } else {
+          const int s = s_first + split_k;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* orow = p.o_acc + ((int64_t)s * p.H + h0 + 16 * hb + 4 * G + r) * kDv + 128 * w + li;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) orow[16 * db] = O[hb][db][r] * ir[r];
+          }
+          if (w == 0 && G == 0) p.lse_acc[(int64_t)s * p.H + h] = lse_out;
+        }
+      }
+      token_start = true;
+    }
+    if (it1.end) break;
+
+    // ---- next sub-tile: convert its staged records, stage the one after, finish the slot ids of k+3
+    __syncthreads();  // the tile and the partials of sub-tile k are no longer read
+    rec_convert(it1, (k + 1) % NSLOT);
+    rec_issue(it2, (k + 2) % NSLOT);
+    idx_finish(it3, (k + 3) % NSLOT);
+    it0 = it1;
+    it1 = it2;
+    it2 = it3;
+    it3 = gen_next<KT>(gen, p);
+    ++k;
+    __syncthreads();  // the converted tile and the new addresses are visible
+  }
+}
+
+template <int DQK, int NH2>
+static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
+  dim3 grid(num_parts, p.H / (16 * NH2));
+  if (precision == 1)
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 1>), grid, dim3(256), 0, stream, p);
+  else if (precision == 2)
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 2>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 3>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
+                                hipStream_t stream) {
+  if (d_qk == 576)
+    return heads_per_group == 16 ? launch_decode_t<576, 1>(p, num_parts, precision, stream)
+                                 : launch_decode_t<576, 2>(p, num_parts, precision, stream);
+  return heads_per_group == 16 ? launch_decode_t<512, 1>(p, num_parts, precision, stream)
+                               : launch_decode_t<512, 2>(p, num_parts, precision, stream);
+}
+
+}  // namespace sda

@@ -92,4 +92,83 @@ __device__ __forceinline__ void split_terms(const float (&v)[8], bf16x8 (&A)[NTE
   }
 }
 
+
+// ---------------------------------------------------------------- global -> LDS streaming helpers
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void gbl_void;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Global -> LDS load of 16 (4) bytes per lane: lane l's bytes land at lds_wave_base + 16 l (4 l);
+// the base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(uint64_t src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(uint64_t src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// Workgroup barrier that does not wait for the gathers in flight (only for this wave's LDS
+// operations). The compiler's __syncthreads would also drain every global -> LDS load.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ds_read_b64_tr_b8 (see lds_read_tr16 for the lane pattern; here 8 one-byte elements from lanes
+// 2e + i / 8). Issued as inline assembly: with the builtin the compiler drains every global -> LDS
+// load in flight before the read, as it cannot tell that the two touch different ring buffers. The
+// result may only be used after an explicit s_waitcnt lgkmcnt that names it as an operand.
+__device__ __forceinline__ i32x2 lds_tr8(uint32_t lds_addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 e4m3 codes -> two bf16x8 (codes 0..7, 8..15), exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 x, bf16x8& lo, bf16x8& hi) {
+  uint32_t y[8];
+  e4m3x4_to_bf16(x[0], y[0], y[1]);
+  e4m3x4_to_bf16(x[1], y[2], y[3]);
+  e4m3x4_to_bf16(x[2], y[4], y[5]);
+  e4m3x4_to_bf16(x[3], y[6], y[7]);
+  lo = __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
+  hi = __builtin_bit_cast(bf16x8, u32x4{y[4], y[5], y[6], y[7]});
+}
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(const i32x2 x) {
+  uint32_t y[4];
+  e4m3x4_to_bf16((uint32_t)x[0], y[0], y[1]);
+  e4m3x4_to_bf16((uint32_t)x[1], y[2], y[3]);
+  return __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
+}
+
+// s_waitcnt vmcnt(N): at most N global operations of this wave still pending (they complete in issue
+// order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until at most n' global operations of this wave are pending, n' the largest step <= n
+// (n is wave-uniform).
+__device__ __forceinline__ void vm_wait_atmost(int n) {
+  if (n >= 32) {
+    if (n >= 48) {
+      if (n >= 56) vm_wait<56>(); else vm_wait<48>();
+    } else {
+      if (n >= 40) vm_wait<40>(); else vm_wait<32>();
+    }
+  } else if (n >= 16) {
+    if (n >= 24) vm_wait<24>(); else vm_wait<16>();
+  } else if (n >= 8) {
+    if (n >= 12) vm_wait<12>(); else vm_wait<8>();
+  } else if (n >= 4) {
+    vm_wait<4>();
+  } else {
+    vm_wait<0>();
+  }
+}
+
 }  // namespace sda

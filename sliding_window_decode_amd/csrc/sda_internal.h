@@ -1,5 +1,5 @@
 // sda_internal.h -- declarations shared by the host API (sda_api.cpp) and the HIP kernels
-// (sda_decode_ring.hip, sda_sched.hip). Not part of the public ABI.
+// (sda_decode_ring.hip, sda_decode_staged.hip, sda_sched.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -94,9 +94,15 @@ __host__ __device__ inline int64_t part_quantum(int64_t total, int num_parts) {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_sched(const SchedParams& p, hipStream_t stream);
-// The decode kernel (sda_decode_ring.hip); launch_decode (sda_api.cpp) forwards to it.
+// The decode kernels: calls without an NVFP4 list run the ring kernel (sda_decode_ring.hip: records
+// streamed into LDS by global -> LDS loads, fp8 widened as read), the others the staged kernel
+// (sda_decode_staged.hip: records staged in registers and widened once into a bf16 tile; up to three
+// workgroups per CU hide the cost of the NVFP4 widening and of the gathers better than one with a deep
+// LDS ring); launch_decode (sda_api.cpp) picks one.
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream);
+hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
+                                hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

@@ -73,8 +73,9 @@ __device__ __forceinline__ void gen_init(ItemGen& g, const DecodeParams& p, int 
   gen_enter(g, p, bt, load_token_info(p, bt));
 }
 
-template <int SUB>
-__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
+// Next item; list L's items have sub[L] rows (64, or 32: tile halves, the second only when it holds
+// rows).
+__device__ __forceinline__ Item gen_next_sub(ItemGen& g, const DecodeParams& p, int sub0, int sub1) {
   Item it;
   if (g.done) {
     it.t = -1;
@@ -91,9 +92,10 @@ __device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
   it.nsplit = g.s1 - g.s0;
   it.L = g.i < g.tm ? 0 : 1;
   it.n = it.L == 0 ? g.n0 : g.n1;
-  it.pos0 = kTileRows * (it.L == 0 ? g.i : g.i - g.tm) + SUB * g.j;
+  const int sub = it.L == 0 ? sub0 : sub1;
+  it.pos0 = kTileRows * (it.L == 0 ? g.i : g.i - g.tm) + sub * g.j;
   it.end = 0;
-  if (SUB < kTileRows && g.j + 1 < kTileRows / SUB && it.pos0 + SUB < it.n) {
+  if (sub < kTileRows && g.j + 1 < kTileRows / sub && it.pos0 + sub < it.n) {
     g.j += 1;
   } else if (g.i + 1 < g.i_end) {
     g.i += 1;
@@ -104,6 +106,11 @@ __device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
     g.done = true;
   }
   return it;
+}
+
+template <int SUB>
+__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
+  return gen_next_sub(g, p, SUB, SUB);
 }
 
 }  // namespace sda
