@@ -159,6 +159,7 @@ def main():
     ap.add_argument("--precision", type=int, default=None, help="override the plan's PV precision (1 or 3)")
     ap.add_argument("--parts", type=int, default=None)
     ap.add_argument("--heads-per-group", type=int, default=None)
+    ap.add_argument("--fixed-overhead", type=int, default=None, help="override the plan's per-token tile overhead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true", help="also time with rotating buffer sets larger than the MALL")
     ap.add_argument("--copy-calib", action="store_true",
@@ -193,6 +194,8 @@ def main():
         plan.num_parts = args.parts
     if args.heads_per_group is not None:
         plan.heads_per_group = args.heads_per_group
+    if args.fixed_overhead is not None:
+        plan.fixed_overhead = args.fixed_overhead
     dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
     out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")

@@ -106,6 +106,8 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
 }
 
 // One workgroup per (token, block of 16 heads); thread (head h = tid / 16, 32 dims from 32 * (tid % 16)).
+// The splits are read four at a time with every load of a batch issued before any is used (a token
+// rarely has more than a few splits), so a merge costs about one global round trip per batch.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int t = blockIdx.x;
   const int s0 = p.num_splits[t];
@@ -116,26 +118,50 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int d0 = 32 * (tid & 15);
   const bool has_sink = p.sink != nullptr;
   const float sk = has_sink ? p.sink[h] : kNegInf;
-  float M = sk;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, p.lse_acc[(int64_t)(s0 + k) * p.H + h]);
   uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + d0;
+  constexpr int KB = 4;  // splits per batch
+  // running merge state: max M, denominator den and accumulator relative to M
+  float M = sk;
+  float den = has_sink ? 1.0f : 0.0f;  // exp(sk - M) with M = sk
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += KB) {
+    float lk[KB];
+    f32x4 v[KB][8];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int k = k0 + j < n ? k0 + j : k0;  // a duplicate read beyond the end, weighted 0 below
+      lk[j] = p.lse_acc[(int64_t)(s0 + k) * p.H + h];
+      const f32x4* src = (const f32x4*)(p.o_acc + ((int64_t)(s0 + k) * p.H + h) * kDv + d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = src[e];
+    }
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (k0 + j < n) bm = fmaxf(bm, lk[j]);
+    if (bm == kNegInf || bm == kPosInf) {
+      M = bm;
+      continue;
+    }
+    const float r = (M == kNegInf) ? 0.f : expf(M - bm);  // rescale what was merged so far
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const float wj = (k0 + j < n && lk[j] != kNegInf) ? expf(lk[j] - bm) : 0.f;
+      den += wj;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wj * v[j][e];
+    }
+    M = bm;
+  }
   if (M == kNegInf || M == kPosInf) {
     for (int e = 0; e < 32; e += 8) *(u32x4*)(orow + e) = u32x4{0u, 0u, 0u, 0u};
     if ((tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = M;
     return;
-  }
-  float den = has_sink ? expf(sk - M) : 0.f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n; ++k) {
-    const float lk = p.lse_acc[(int64_t)(s0 + k) * p.H + h];
-    if (lk == kNegInf) continue;
-    const float w = expf(lk - M);
-    den += w;
-    const f32x4* src = (const f32x4*)(p.o_acc + ((int64_t)(s0 + k) * p.H + h) * kDv + d0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += w * src[e];
   }
   const float inv = 1.0f / den;
 #pragma unroll
