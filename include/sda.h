@@ -129,9 +129,11 @@ size_t sda_workspace_bytes(int T, int H, int d_v, const sda_plan* plan /*host*/)
  * tiles of 64 list positions plus plan->fixed_overhead, and cuts the concatenated (token, tile)
  * sequence into plan->num_parts contiguous parts of near-equal cost.
  * Writes meta [num_parts][SDA_META_INTS] int32:
- *   {begin_token, begin_tile, end_token, end_tile, begin_split, 0, 0, 0}
+ *   {begin_token, begin_tile, end_token, end_tile, begin_split, n_main, n_extra, first_split}
  * (a part covers the tiles from (begin_token, begin_tile) up to, not including, (end_token,
- * end_tile); begin_split is the index of this part among the parts that touch begin_token) and
+ * end_tile); begin_split is the index of this part among the parts that touch begin_token; n_main
+ * and n_extra are begin_token's list lengths clamped to [0, width] and first_split is
+ * num_splits[begin_token]; parts with no tiles hold {T, 0, T, 0, 0, 0, 0, 0}) and
  * num_splits [T+1] int32, the exclusive prefix sum of the number of parts that touch each token.
  * The result depends only on the lengths, so one call can serve every layer of a decode step.
  * extra may be NULL. */

@@ -268,7 +268,9 @@ int sda_get_sched_meta_host(int T, const int32_t* lens, int width, const int32_t
       m[0] = t;
       m[1] = (int32_t)bi;
       m[4] = pp >= p0 ? (int32_t)(pp - p0) : 0;
-      m[5] = m[6] = m[7] = 0;
+      m[5] = n0;
+      m[6] = n1;
+      m[7] = num_splits[t];
       if (pp > 0) {
         meta[(pp - 1) * SDA_META_INTS + 2] = t;
         meta[(pp - 1) * SDA_META_INTS + 3] = (int32_t)bi;

@@ -76,7 +76,10 @@ void decode_ring_kernel(DecodeParams p) {
   // list parameters are read from the kernel arguments where used (scalar loads), not held in registers
   auto LD = [&](int L) -> const ListDev& { return p.lst[L]; };
   const int32_t* mt = p.meta + (int64_t)blockIdx.x * SDA_META_INTS;
-  const int bt = mt[0], bi = mt[1], et = mt[2], ei = mt[3], bk = mt[4];
+  int32_t mrec[SDA_META_INTS];
+#pragma unroll
+  for (int i = 0; i < SDA_META_INTS; ++i) mrec[i] = mt[i];
+  const int bt = mrec[0], bi = mrec[1], et = mrec[2], ei = mrec[3], bk = mrec[4];
   if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
 
   const float sink2 = p.sink ? p.sink[h0 + li] * kLog2e : kNegInf;  // head li's sink logit, log2 units
@@ -84,7 +87,7 @@ void decode_ring_kernel(DecodeParams p) {
   // ---- slot ids -> record addresses, for the RW rows this wave gathers (lane l: row RW w + l % RW)
   auto load_sid = [&](const Item& it) -> int {
     int sid = -1;
-    if (!it.end) {
+    if (!it.end()) {
       const int pos = it.pos0 + RW * w + lane % RW;
       const ListDev& ld = LD(it.L);
       if (pos < it.n) sid = ld.idx[(int64_t)it.t * ld.row_stride + pos];
@@ -128,10 +131,11 @@ void decode_ring_kernel(DecodeParams p) {
 
   // ---- prologue: items k = 0 .. NB, gathers of tiles 0 .. NB-2 in flight, slot ids of tile NB-1
   ItemGen gen;
-  gen_init(gen, p, bt, bi, et, ei);
+  TokenInfoRegs tinfo;
+  gen_init(gen, p, tinfo, mrec);
   Item its[NB + 1];  // its[j] = tile k + j
 #pragma unroll
-  for (int j = 0; j <= NB; ++j) its[j] = gen_next<kTileRows>(gen, p);
+  for (int j = 0; j <= NB; ++j) its[j] = gen_next<kTileRows>(gen, p, tinfo);
   int sid_next;
   {
     int sids[NB];
@@ -139,7 +143,7 @@ void decode_ring_kernel(DecodeParams p) {
     for (int j = 0; j < NB; ++j) sids[j] = load_sid(its[j]);  // every slot id load before any gather
 #pragma unroll
     for (int j = 0; j + 1 < NB; ++j) {
-      if (!its[j].end) {
+      if (!its[j].end()) {
         const uint32_t vm = gather(its[j], sids[j], j);
         if (lane == 0) sm.vmask[j][w] = vm;
       }
@@ -174,12 +178,12 @@ void decode_ring_kernel(DecodeParams p) {
   reset_state();
 
   // ---- output of token t (its last tile in this part is done)
-  auto epilogue = [&](int t, int s_first, int nsplit) {
+  auto epilogue = [&](int t, int s_first, bool whole) {
     const int split_k = (t == bt) ? bk : 0;
     const float lt = sum_across_groups(l);
     const int h = h0 + li;
     float inv, lse_out;
-    if (nsplit <= 1) {
+    if (whole) {
       const float Mx = fmaxf(m, sink2);
       if (Mx == kNegInf) {
         inv = 0.f;
@@ -200,7 +204,7 @@ void decode_ring_kernel(DecodeParams p) {
     float ir[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * G + r);
-    if (nsplit <= 1) {
+    if (whole) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)(h0 + 4 * G + r) * p.o_sh + 128 * wr + li;
@@ -241,11 +245,11 @@ void decode_ring_kernel(DecodeParams p) {
     cnt_iter[r] = 0;
     cnt_tail[r] = QN;
 #pragma unroll
-    for (int i2 = r + 1; i2 + 1 < NB; ++i2) cnt_tail[r] += its[i2].end ? 0 : NI;
+    for (int i2 = r + 1; i2 + 1 < NB; ++i2) cnt_tail[r] += its[i2].end() ? 0 : NI;
   }
 
   int k = 0;
-  int ep_t = -1, ep_s = 0, ep_n = 0;  // token whose output is pending, its split range
+  int ep_t = -1, ep_s = 0, ep_n = 1;  // token whose output is pending, its first split, whether whole
   while (true) {
     const int b = k % NB;
     // Tile k landed once this wave has at most as many global ops pending as it issued after the
@@ -267,7 +271,7 @@ void decode_ring_kernel(DecodeParams p) {
     }
     // slot ids of tile k+NB, then the gather of tile k+NB-1 into the free buffer
     const int sid_new = load_sid(its[NB]);
-    if (!its[NB - 1].end) {
+    if (!its[NB - 1].end()) {
       const int bg = (k + NB - 1) % NB;
       const uint32_t vm = gather(its[NB - 1], sid_next, bg);
       if (lane == 0) sm.vmask[bg][w] = vm;
@@ -337,7 +341,7 @@ void decode_ring_kernel(DecodeParams p) {
     barrier_lds();  // scores of all rows visible
 
     // Q of the next tile's token (the registers are free until its QK^T)
-    if (!it1.end && it1.t != it0.t) {
+    if (!it1.end() && it1.t != it0.t) {
       load_q(it1.t);
       c_iter += QN;
       c_tail = QN;
@@ -450,12 +454,12 @@ void decode_ring_kernel(DecodeParams p) {
       mma_half(1);
     }
 
-    if (it1.end || it1.t != it0.t) {
+    if (it1.end() || it1.t != it0.t) {
       ep_t = it0.t;
       ep_s = it0.s_first;
-      ep_n = it0.nsplit;
+      ep_n = it0.whole;
     }
-    if (it1.end) break;
+    if (it1.end()) break;
 #pragma unroll
     for (int r = 0; r + 2 < NB; ++r) {
       cnt_iter[r] = cnt_iter[r + 1];
@@ -465,7 +469,7 @@ void decode_ring_kernel(DecodeParams p) {
     cnt_tail[NB - 2] = c_tail;
 #pragma unroll
     for (int j = 0; j < NB; ++j) its[j] = its[j + 1];
-    its[NB] = gen_next<kTileRows>(gen, p);
+    its[NB] = gen_next<kTileRows>(gen, p, tinfo);
     ++k;
   }
   if (ep_t >= 0) epilogue(ep_t, ep_s, ep_n);

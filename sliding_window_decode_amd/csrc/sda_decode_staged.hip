@@ -86,7 +86,7 @@ void decode_kernel(DecodeParams p) {
   int pf_sid = -1;
   auto idx_issue = [&](const Item& it) {
     pf_sid = -1;
-    if (!it.end && tid < KT) {
+    if (!it.end() && tid < KT) {
       const int pos = it.pos0 + tid;
       if (pos < it.n) pf_sid = LD(it.L).idx[(int64_t)it.t * LD(it.L).row_stride + pos];
     }
@@ -94,7 +94,7 @@ void decode_kernel(DecodeParams p) {
   auto idx_finish = [&](const Item& it, int s) {
     if (w == 0) {
       const ListDev& ld = LD(it.L);
-      const bool ok = !it.end && tid < KT && pf_sid >= 0 && pf_sid < ld.slots;
+      const bool ok = !it.end() && tid < KT && pf_sid >= 0 && pf_sid < ld.slots;
       uint64_t a = 0, sa = 0;
       if (ok) {
         const uint32_t pg = (uint32_t)pf_sid >> ld.page_shift;
@@ -117,7 +117,7 @@ void decode_kernel(DecodeParams p) {
   u32x4 stg_sc;
   u32x4 stg_rp;
   auto rec_issue = [&](const Item& it, int s) {
-    if (it.end || !sm.slot_any[s]) return;
+    if (it.end() || !sm.slot_any[s]) return;
     const ListDev& ld = LD(it.L);
     const uint64_t dummy = (uint64_t)ld.base;
     if (ld.format == SDA_NVFP4_288) {
@@ -149,7 +149,7 @@ void decode_kernel(DecodeParams p) {
     }
   };
   auto rec_convert = [&](const Item& it, int s) {
-    const bool live = !it.end && sm.slot_any[s];
+    const bool live = !it.end() && sm.slot_any[s];
     if (tid == 0) sm.tile_any = live ? 1 : 0;
     if (!live) return;
     const ListDev& ld = LD(it.L);
@@ -218,11 +218,12 @@ void decode_kernel(DecodeParams p) {
 
   // ---- prologue: items k = 0..3, addresses of 0..2, records of 0 converted, records of 1 in flight
   ItemGen gen;
-  gen_init(gen, p, bt, bi, et, ei);
-  Item it0 = gen_next<KT>(gen, p);
-  Item it1 = gen_next<KT>(gen, p);
-  Item it2 = gen_next<KT>(gen, p);
-  Item it3 = gen_next<KT>(gen, p);
+  TokenInfoRegs tinfo;
+  gen_init(gen, p, tinfo, mt);
+  Item it0 = gen_next<KT>(gen, p, tinfo);
+  Item it1 = gen_next<KT>(gen, p, tinfo);
+  Item it2 = gen_next<KT>(gen, p, tinfo);
+  Item it3 = gen_next<KT>(gen, p, tinfo);
   idx_issue(it0);
   idx_finish(it0, 0);
   idx_issue(it1);
@@ -361,17 +362,17 @@ void decode_kernel(DecodeParams p) {
     }
 
     // ---- epilogue after the token's last sub-tile in this part
-    if (it1.end || it1.t != it0.t) {
+    if (it1.end() || it1.t != it0.t) {
       const int t = it0.t;
       const int s_first = it0.s_first;
-      const int nsplit = it0.nsplit;
+      const bool whole = it0.whole;
       const int split_k = (t == bt) ? bk : 0;
 #pragma unroll
       for (int hb = 0; hb < NH2; ++hb) {
         const float lt = sum_across_groups(l[hb]);
         const int h = h0 + 16 * hb + li;
         float inv, lse_out;
-        if (nsplit <= 1) {
+        if (whole) {
           const bool has_sink = p.sink != nullptr;
           const float s2 = has_sink ? p.sink[h] * kLog2e : kNegInf;
           const float Mx = fmaxf(m[hb], s2);
@@ -394,7 +395,7 @@ void decode_kernel(DecodeParams p) {
         float ir[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * G + r);
-        if (nsplit <= 1) {
+        if (whole) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)(h0 + 16 * hb + 4 * G + r) * p.o_sh + 128 * w + li;
@@ -415,7 +416,7 @@ void decode_kernel(DecodeParams p) {
       }
       token_start = true;
     }
-    if (it1.end) break;
+    if (it1.end()) break;
 
     // ---- next sub-tile: convert its staged records, stage the one after, finish the slot ids of k+3
     __syncthreads();  // the tile and the partials of sub-tile k are no longer read
@@ -425,7 +426,7 @@ void decode_kernel(DecodeParams p) {
     it0 = it1;
     it1 = it2;
     it2 = it3;
-    it3 = gen_next<KT>(gen, p);
+    it3 = gen_next<KT>(gen, p, tinfo);
     ++k;
     __syncthreads();  // the converted tile and the new addresses are visible
   }

@@ -126,6 +126,34 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Global stores issued as inline assembly. The compiler then sees only loads among this wave's
+// pending vector-memory operations, and counts them exactly where it must wait for one (pending loads
+// and stores together make it wait for all of them). A wait on a load must then count loads only:
+// stores may complete in any order relative to loads.
+__device__ __forceinline__ void st_global_u16(void* p, uint32_t v) {
+  asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_global_f32(void* p, float v) {
+  asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+// 16-byte global load the compiler does not track: r receives the data when the load completes.
+// The caller must wait for it by count (vmcnt) and then name r as an operand of an inline-assembly
+// statement, so that no use of r is placed above the wait. r is tied to its previous register, so
+// the load lands where r already lives.
+__device__ __forceinline__ void ld_global_b128_untracked(bf16x8& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(r) : "v"(p) : "memory");
+}
+
+// ds_read_b32 and its wait in one statement, so the value is complete when the statement ends. For
+// words written by a global -> LDS load, after an explicit vmcnt wait: the compiler does not see
+// that dependence, and a builtin read would make it drain every such load in flight instead.
+__device__ __forceinline__ int lds_ld_i32(uint32_t lds_addr) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr) : "memory");
+  return r;
+}
+
 // 16 e4m3 codes -> two bf16x8 (codes 0..7, 8..15), exact.
 __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 x, bf16x8& lo, bf16x8& hi) {
   uint32_t y[8];
@@ -151,24 +179,26 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Waits until at most n' global operations of this wave are pending, n' the largest step <= n
-// (n is wave-uniform).
-__device__ __forceinline__ void vm_wait_atmost(int n) {
-  if (n >= 32) {
-    if (n >= 48) {
-      if (n >= 56) vm_wait<56>(); else vm_wait<48>();
-    } else {
-      if (n >= 40) vm_wait<40>(); else vm_wait<32>();
-    }
-  } else if (n >= 16) {
-    if (n >= 24) vm_wait<24>(); else vm_wait<16>();
-  } else if (n >= 8) {
-    if (n >= 12) vm_wait<12>(); else vm_wait<8>();
-  } else if (n >= 4) {
-    vm_wait<4>();
+template <int LO, int HI>
+__device__ __forceinline__ void vm_wait_tree(int n) {
+  if constexpr (LO == HI) {
+    vm_wait<LO>();
   } else {
-    vm_wait<0>();
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID)
+      vm_wait_tree<MID, HI>(n);
+    else
+      vm_wait_tree<LO, MID - 1>(n);
   }
+}
+
+// Waits until at most n global operations of this wave are pending (n is wave-uniform): exactly n up
+// to 31, and 32 for larger n (then more is waited for than needed, never less).
+__device__ __forceinline__ void vm_wait_atmost(int n) {
+  if (n >= 32)
+    vm_wait<32>();
+  else
+    vm_wait_tree<0, 31>(n);
 }
 
 }  // namespace sda

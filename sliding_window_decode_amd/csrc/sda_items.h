@@ -5,25 +5,30 @@
 // first the ceil(n_main/64) tiles of its main list, then those of its extra list; a token with no
 // rows still has one (empty) tile so that its output is written. A kernel may walk each 64-row tile
 // as SUB-row items (SUB = 32: two halves, the second only when it holds rows).
+//
+// The part's first token comes with its lengths and split index in the meta record, so that walking
+// starts without a memory round trip. The lengths and split index of each later token are fetched
+// when the walker enters the token before it, through a source the kernel chooses (registers, or
+// LDS filled by a global -> LDS load), so that they have long arrived when they are used.
 #pragma once
 
+#include "sda_device.h"
 #include "sda_internal.h"
 
 namespace sda {
 
-// One item, as wave-uniform scalars: token, list, first list position, list length, end marker, and
-// the token's split range (first split index, number of splits).
+// One item, as wave-uniform scalars: token (-1 past the part's end), list, first list position, list
+// length, the token's first split index, and whether this part holds all of the token's tiles (its
+// output is then final; otherwise it is one split of the token, number s_first + begin_split for the
+// part's first token and s_first for any other).
 struct Item {
-  int t, L, pos0, n, end, s_first, nsplit;
+  int t, L, pos0, n, s_first, whole;
+  __device__ __forceinline__ bool end() const { return t < 0; }
 };
 
-// The lengths and split range of the next token are loaded when the walker enters a token, so that
-// the loads are long complete when they are used (a load consumed right away would make the wave
-// wait for every global load in flight, the gathers included). The raw values stay in vector
-// registers until then: the load index carries an opaque zero so that the compiler does not move
-// them to scalar registers (which needs the load to be complete) straight after the load.
+// Raw lengths of both lists (or their widths) and num_splits[t] of a token.
 struct TokenInfo {
-  int r0, r1, s0, s1;  // raw lens of both lists (or their widths), num_splits[t], num_splits[t + 1]
+  int r0, r1, s0;
 };
 
 __device__ __forceinline__ int opaque_lane_zero() {
@@ -32,85 +37,126 @@ __device__ __forceinline__ int opaque_lane_zero() {
   return z;
 }
 
+// Token information in registers. The load index carries an opaque zero so that the compiler keeps
+// the raw values in vector registers (moving them to scalar registers needs the loads complete)
+// until the walker enters the token.
+struct TokenInfoRegs {
+  TokenInfo x;
+  __device__ __forceinline__ void issue(const DecodeParams& p, int t) {
+    const int tz = t + opaque_lane_zero();
+    x.r0 = p.lst[0].lens ? p.lst[0].lens[tz] : p.lst[0].width;
+    x.r1 = p.nlists > 1 ? (p.lst[1].lens ? p.lst[1].lens[tz] : p.lst[1].width) : 0;
+    x.s0 = p.num_splits[tz];
+  }
+  __device__ __forceinline__ TokenInfo fetch(const DecodeParams&) const { return x; }
+};
+
+// Token information through LDS: lanes 0..2 of the wave load the three words into `buf` (this
+// wave's 16 bytes, two alternating slots). The caller must wait for the load (one global operation;
+// `fresh` is set when one is issued) before the walker fetches it.
+struct TokenInfoLds {
+  int32_t* buf;  // [2][4] words of this wave
+  int slot;
+  int fresh;
+  __device__ __forceinline__ void issue(const DecodeParams& p, int t) {
+    const int lane = threadIdx.x & 63;
+    slot ^= 1;
+    const int32_t* src = p.num_splits + t;  // lane 2; also read (and not used) by lanes 0, 1 without lengths
+    if (lane == 0 && p.lst[0].lens) src = p.lst[0].lens + t;
+    if (lane == 1 && p.nlists > 1 && p.lst[1].lens) src = p.lst[1].lens + t;
+    if (lane < 3) dma4((uint64_t)src, buf + 4 * slot);
+    fresh = 1;
+  }
+  __device__ __forceinline__ TokenInfo fetch(const DecodeParams& p) const {
+    const uint32_t a = lds_u32(buf + 4 * slot);
+    TokenInfo x;
+    x.r0 = p.lst[0].lens ? lds_ld_i32(a) : p.lst[0].width;
+    x.r1 = p.nlists > 1 ? (p.lst[1].lens ? lds_ld_i32(a + 4) : p.lst[1].width) : 0;
+    x.s0 = lds_ld_i32(a + 8);
+    return x;
+  }
+};
+
 struct ItemGen {
-  int t, i, j, n0, n1, tm, i_end, t_last, bt, bi, et, ei, s0, s1;
-  TokenInfo next;
+  int t, i, j, n0, n1, tm, i_end, t_last, bt, bi, et, ei, s0;
   bool done;
 };
 
-__device__ __forceinline__ TokenInfo load_token_info(const DecodeParams& p, int t) {
-  const int tz = t + opaque_lane_zero();
-  TokenInfo x;
-  x.r0 = p.lst[0].lens ? p.lst[0].lens[tz] : p.lst[0].width;
-  x.r1 = p.nlists > 1 ? (p.lst[1].lens ? p.lst[1].lens[tz] : p.lst[1].width) : 0;
-  x.s0 = p.num_splits[tz];
-  x.s1 = p.num_splits[tz + 1];
-  return x;
-}
-
 __device__ __forceinline__ int clamp_raw(int n, int width) { return n < 0 ? 0 : (n > width ? width : n); }
 
-__device__ __forceinline__ void gen_enter(ItemGen& g, const DecodeParams& p, int t, const TokenInfo& x) {
+template <class Src>
+__device__ __forceinline__ void gen_enter(ItemGen& g, const DecodeParams& p, Src& src, int t, int r0, int r1, int s0) {
   g.t = t;
-  g.n0 = clamp_raw(__builtin_amdgcn_readfirstlane(x.r0), p.lst[0].width);
-  g.n1 = p.nlists > 1 ? clamp_raw(__builtin_amdgcn_readfirstlane(x.r1), p.lst[1].width) : 0;
-  g.s0 = __builtin_amdgcn_readfirstlane(x.s0);
-  g.s1 = __builtin_amdgcn_readfirstlane(x.s1);
+  g.n0 = clamp_raw(r0, p.lst[0].width);
+  g.n1 = p.nlists > 1 ? clamp_raw(r1, p.lst[1].width) : 0;
+  g.s0 = s0;
   g.tm = (g.n0 + kTileRows - 1) / kTileRows;
   g.i = (t == g.bt) ? g.bi : 0;
   g.j = 0;
   g.i_end = (t == g.et) ? g.ei : token_tiles(g.n0, g.n1);
-  if (t + 1 <= g.t_last && t + 1 < p.T) g.next = load_token_info(p, t + 1);
+  if (t + 1 <= g.t_last && t + 1 < p.T) src.issue(p, t + 1);
 }
 
-__device__ __forceinline__ void gen_init(ItemGen& g, const DecodeParams& p, int bt, int bi, int et, int ei) {
-  g.bt = bt;
-  g.bi = bi;
-  g.et = et;
-  g.ei = ei;
-  g.t_last = (ei > 0) ? et : et - 1;
+// Starts at the part of meta record m (begin token, begin tile, end token, end tile, begin split,
+// clamped main and extra lengths of the begin token, num_splits[begin token]).
+template <class Src>
+__device__ __forceinline__ void gen_init(ItemGen& g, const DecodeParams& p, Src& src, const int32_t* m) {
+  g.bt = m[0];
+  g.bi = m[1];
+  g.et = m[2];
+  g.ei = m[3];
+  g.t_last = (g.ei > 0) ? g.et : g.et - 1;
   g.done = false;
-  gen_enter(g, p, bt, load_token_info(p, bt));
+  gen_enter(g, p, src, g.bt, m[5], m[6], m[7]);
 }
 
 // Next item; list L's items have sub[L] rows (64, or 32: tile halves, the second only when it holds
 // rows).
-__device__ __forceinline__ Item gen_next_sub(ItemGen& g, const DecodeParams& p, int sub0, int sub1) {
+// before_fetch() runs just before the walker reads a token's fetched information.
+template <class Src, class Wait>
+__device__ __forceinline__ Item gen_next_sub(ItemGen& g, const DecodeParams& p, Src& src, int sub0, int sub1,
+                                             Wait&& before_fetch) {
   Item it;
   if (g.done) {
     it.t = -1;
     it.L = 0;
     it.pos0 = 0;
     it.n = 0;
-    it.end = 1;
     it.s_first = 0;
-    it.nsplit = 0;
+    it.whole = 1;
     return it;
   }
   it.t = g.t;
   it.s_first = g.s0;
-  it.nsplit = g.s1 - g.s0;
+  it.whole = (g.t != g.bt || g.bi == 0) && (g.t != g.et || g.ei == 0);
   it.L = g.i < g.tm ? 0 : 1;
   it.n = it.L == 0 ? g.n0 : g.n1;
   const int sub = it.L == 0 ? sub0 : sub1;
   it.pos0 = kTileRows * (it.L == 0 ? g.i : g.i - g.tm) + sub * g.j;
-  it.end = 0;
   if (sub < kTileRows && g.j + 1 < kTileRows / sub && it.pos0 + sub < it.n) {
     g.j += 1;
   } else if (g.i + 1 < g.i_end) {
     g.i += 1;
     g.j = 0;
   } else if (g.t + 1 <= g.t_last && g.t + 1 < p.T) {
-    gen_enter(g, p, g.t + 1, g.next);
+    before_fetch();
+    const TokenInfo x = src.fetch(p);
+    gen_enter(g, p, src, g.t + 1, __builtin_amdgcn_readfirstlane(x.r0), __builtin_amdgcn_readfirstlane(x.r1),
+              __builtin_amdgcn_readfirstlane(x.s0));
   } else {
     g.done = true;
   }
   return it;
 }
 
-template <int SUB>
-__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p) {
-  return gen_next_sub(g, p, SUB, SUB);
+template <int SUB, class Src>
+__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p, Src& src) {
+  return gen_next_sub(g, p, src, SUB, SUB, [] {});
+}
+
+template <int SUB, class Src, class Wait>
+__device__ __forceinline__ Item gen_next(ItemGen& g, const DecodeParams& p, Src& src, Wait&& before_fetch) {
+  return gen_next_sub(g, p, src, SUB, SUB, before_fetch);
 }
 
 }  // namespace sda

@@ -52,10 +52,10 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
   int carry = 0, split_carry = 0;
   for (int base = 0; base < p.T; base += NT) {
     const int t = base + tid;
-    int nt = 0, cost = 0;
+    int nt = 0, cost = 0, n0 = 0, n1 = 0;
     if (t < p.T) {
-      const int n0 = clamp_len(p.lens[0], p.width[0], t);
-      const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
+      n0 = clamp_len(p.lens[0], p.width[0], t);
+      n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
       nt = token_tiles(n0, n1);
       cost = nt + p.F;
     }
@@ -71,7 +71,8 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
     int chunk_splits = 0;
     const int sincl = block_incl_scan(nsplit, wave_tot, chunk_splits);
     if (t < p.T) {
-      p.num_splits[t] = split_carry + sincl - nsplit;
+      const int s_first = split_carry + sincl - nsplit;
+      p.num_splits[t] = s_first;
       const int prev_last = (cum == 0) ? -1 : (cum - 1) / Q;  // part of the previous token's last tile
       for (int pp = prev_last + 1; pp <= p1; ++pp) {
         const int bi = pp * Q - pos0 > 0 ? pp * Q - pos0 : 0;
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
         m[0] = t;
         m[1] = bi;
         m[4] = (pp >= p0) ? pp - p0 : 0;
-        m[5] = 0;
-        m[6] = 0;
-        m[7] = 0;
+        m[5] = n0;
+        m[6] = n1;
+        m[7] = s_first;
         if (pp > 0) {
           int32_t* mp = p.meta + (int64_t)(pp - 1) * SDA_META_INTS;
           mp[2] = t;

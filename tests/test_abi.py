@@ -192,6 +192,18 @@ def _check_schedule(meta, ns, T, n0, n1, P):
             bt = meta[p, 0]
             if bt == t:
                 assert first_k[p] == k
+    for p in range(P):
+        bt, bi, et, ei = meta[p, :4]
+        if bt < T:
+            # the begin token's clamped lengths and first split index travel in the record
+            assert (meta[p, 5], meta[p, 6], meta[p, 7]) == (n0[bt], n1[bt], ns[bt])
+            # a part holds the whole of a token it touches exactly when the token has one split:
+            # it starts at the token's first tile (or before) and ends after its last one
+            for t in range(bt, min(et + (1 if ei > 0 else 0), T)):
+                whole = (t != bt or bi == 0) and (t != et or ei == 0)
+                assert whole == (nsplit[t] == 1)
+        else:
+            assert list(meta[p]) == [T, 0, T, 0, 0, 0, 0, 0]
 
 
 @pytest.mark.parametrize("seed", range(6))
