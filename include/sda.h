@@ -92,8 +92,8 @@ typedef struct sda_list {
 } sda_list;
 
 /* How one decode call is cut across the GPU. Filled by sda_make_plan (host only, no device access);
- * callers may adjust num_parts (>= 1) and heads_per_group (16 or 32, dividing H) for tuning --
- * results do not depend on either beyond fp32 summation order.
+ * callers may adjust num_parts (>= 1) and heads_per_group (16, 32 or 64, dividing H; calls with an
+ * NVFP4 list use at most 32) for tuning -- results do not depend on either beyond fp32 summation order.
  *  num_parts        scheduler parts: rows of the meta array (FlashMLA DecodeImplMeta.num_sm_parts)
  *  heads_per_group  query heads one workgroup computes; the grid is num_parts x H/heads_per_group
  *  fixed_overhead   scheduler cost of starting a token inside a part, in 64-row tiles

@@ -85,8 +85,8 @@ int check_plan(const sda_plan* plan, int H) {
   if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->num_parts < 1 || plan->num_parts > (1 << 20)) return fail(SDA_ERR_INVALID_ARG, "plan.num_parts out of range");
   const int hb = plan->heads_per_group;
-  if (!(hb == 16 || hb == 32) || H % hb != 0)
-    return fail(SDA_ERR_UNSUPPORTED, "plan.heads_per_group must be 16 or 32 and divide H");
+  if (!(hb == 16 || hb == 32 || hb == 64) || H % hb != 0)
+    return fail(SDA_ERR_UNSUPPORTED, "plan.heads_per_group must be 16, 32 or 64 and divide H");
   if (plan->fixed_overhead < 0 || plan->fixed_overhead > 1024)
     return fail(SDA_ERR_INVALID_ARG, "plan.fixed_overhead out of range");
   if (plan->precision < 1 || plan->precision > 3) return fail(SDA_ERR_INVALID_ARG, "plan.precision must be 1, 2 or 3");
@@ -131,7 +131,8 @@ namespace sda {
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream) {
   const bool fp4 = p.lst[0].format == SDA_NVFP4_288 || (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288);
-  return fp4 ? launch_decode_staged(p, num_parts, heads_per_group, d_qk, precision, stream)
+  // the register-staged kernel takes at most 32 heads per workgroup
+  return fp4 ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision, stream)
              : launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
 }
 }  // namespace sda
@@ -201,11 +202,12 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
   if (d_qk != 512 && d_qk != 576) return fail(SDA_ERR_UNSUPPORTED, "d_qk must be 512 or 576");
   if (num_cus <= 0) num_cus = 256;
-  // Heads per workgroup: 32 when H allows it (eight waves, one workgroup per CU, every record read once
-  // per 32 heads), else 16 (four waves; two workgroups per CU for fp8 records, three for NVFP4 ones:
-  // three parts per CU). The parts fill every workgroup slot once; a part's head groups land on the
-  // same XCD (shared L2) when num_parts % 8 == 0.
-  const int hb = H >= 32 ? 32 : 16;
+  // Heads per workgroup: 64 for 576-dim records when H allows it (eight waves, one workgroup per CU,
+  // every record gathered once per 64 heads: the long top-k lists are bound by the gathers), else 32
+  // when H allows it (eight waves, one workgroup per CU), else 16 (four waves; two workgroups per CU
+  // for fp8 records, three for NVFP4 ones: three parts per CU). The parts fill every workgroup slot
+  // once; a part's head groups land on the same XCD (shared L2) when num_parts % 8 == 0.
+  const int hb = (d_qk == 576 && H >= 64) ? 64 : (H >= 32 ? 32 : 16);
   const int groups = H / hb;
   const int slots_per_cu = (hb == 16 && d_qk == 512) ? 3 : 1;
   int parts = (slots_per_cu * num_cus) / groups;

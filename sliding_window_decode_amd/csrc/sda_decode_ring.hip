@@ -43,33 +43,52 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_record[1024];
 
 }  // namespace
 
+// Waves of a workgroup with HS head sets: four per set up to 32 heads, eight for 64 heads.
+template <int HS>
+struct RingShape {
+  static constexpr int NW = HS == 4 ? 8 : 4 * HS;  // waves
+  static constexpr int WPS = NW / HS;              // waves per head set (4 or 2)
+  static constexpr int NRB = 4 / WPS;              // 16-row blocks of a wave's QK^T (1 or 2)
+  static constexpr int NDG = 4 / WPS;              // 128-dim groups of a wave's PV (1 or 2)
+  static constexpr int RW = kTileRows / NW;        // rows gathered by each wave
+  // QK^T: with up to 32 heads a wave takes 16 NRB rows over all dims; with 64 heads the two waves of a
+  // head set split the dims instead (all 64 rows, two 128-dim groups and half the rope dims each),
+  // which halves the Q registers, and their partial scores are summed when read
+  static constexpr bool kDimSplit = HS == 4;
+  static constexpr int NPART = kDimSplit ? 2 : 1;  // partial score arrays
+};
+
 template <int DQK, int HS, int NB>
 struct RingSmem {
   static constexpr int RS = DQK == 576 ? 656 : 528;  // ring row stride in bytes (odd number of chunks)
+  static constexpr int NW = RingShape<HS>::NW;
   char ring[NB][kTileRows * RS];
-  f32x4 sx[HS][4][64];          // scores of each wave's 16 rows, MFMA output layout
+  f32x4 sx[RingShape<HS>::NPART][HS][4][64];  // (partial) scores per 16-row block and head set, MFMA layout
   float sscale[NB][64];         // per-slot scales (FP8_SLOTSCALE)
   float vs[4][64];              // per dim group: its scale for every row of the tile
-  uint32_t vmask[NB][4 * HS];   // valid rows of each ring buffer, one mask per gathering wave
-  uint64_t raddr[4 * HS][16 / HS];  // per wave: record addresses of the rows it gathers
+  uint32_t vmask[NB][NW];       // valid rows of each ring buffer, one mask per gathering wave
+  uint64_t raddr[NW][RingShape<HS>::RW];  // per wave: record addresses of the rows it gathers
 };
 
-// HS head sets of 16 heads per workgroup (4 HS waves), NB ring buffers (tiles k+1 .. k+NB-1 in flight
-// while tile k is computed), NTERM bf16 terms of P'.
+// HS head sets of 16 heads per workgroup (HS = 1, 2, 4: 16, 32 or 64 heads), NB ring buffers (tiles
+// k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'.
 template <int DQK, int HS, int NTERM, int NB>
-__global__ __launch_bounds__(256 * HS) __attribute__((amdgpu_waves_per_eu(HS == 2 || (DQK == 512 && NB == 2) ? 2 : 1)))
+__global__ __launch_bounds__(64 * RingShape<HS>::NW)
+__attribute__((amdgpu_waves_per_eu(RingShape<HS>::NW == 8 || (DQK == 512 && NB == 2) ? 2 : 1)))
 void decode_ring_kernel(DecodeParams p) {
   using Smem = RingSmem<DQK, HS, NB>;
+  using Shape = RingShape<HS>;
   constexpr int RS = Smem::RS;
   constexpr int RSC = RS / 16;                // chunks per ring row
-  constexpr int RW = 16 / HS;                 // rows gathered by each wave
+  constexpr int RW = Shape::RW;               // rows gathered by each wave
+  constexpr int NRB = Shape::NRB, NDG = Shape::NDG;
   constexpr int NI = (RW * RSC + 63) / 64;    // gather instructions per wave and tile
   constexpr bool kRope = DQK == 576;
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int hs = w >> 2, wr = w & 3;          // head set; row block (QK^T) and dim group (PV)
+  const int hs = w / Shape::WPS, sub = w % Shape::WPS;  // head set; its rows (QK^T) and dims (PV)
   const int G = lane >> 4, li = lane & 15;
   const int h0 = blockIdx.y * (16 * HS) + 16 * hs;  // first head of this wave's set
 
@@ -151,27 +170,35 @@ void decode_ring_kernel(DecodeParams p) {
     sid_next = sids[NB - 1];
   }
 
-  bf16x8 qreg[16];  // k-step 2j: dims 64j + 16G + 0..7, k-step 2j+1: dims 64j + 16G + 8..15
-  bf16x8 qrope[2];  // dims 512 + 16G + 0..7 and + 8..15
+  // Q of head h0 + li: the 64-dim blocks qj0 .. qj0 + NQJ - 1 (all eight, or the four of this wave's
+  // half), k-step 2j: dims 64 (qj0 + j) + 16G + 0..7, k-step 2j+1: + 8..15; rope k-steps qr0 .. (dims
+  // 512 + 16G + 8r + 0..7)
+  constexpr bool kDimSplit = Shape::kDimSplit;
+  constexpr int NQJ = kDimSplit ? 4 : 8;
+  constexpr int NQR = kDimSplit ? 1 : 2;
+  const int qj0 = kDimSplit ? 4 * sub : 0;
+  const int qr0 = kDimSplit ? sub : 0;
+  bf16x8 qreg[2 * NQJ];
+  bf16x8 qrope[NQR];
   auto load_q = [&](int t) {
     const uint16_t* qh = p.q + (int64_t)t * p.q_st + (int64_t)(h0 + li) * p.q_sh + 16 * G;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qreg[2 * j] = *(const bf16x8*)(qh + 64 * j);
-      qreg[2 * j + 1] = *(const bf16x8*)(qh + 64 * j + 8);
+    for (int j = 0; j < NQJ; ++j) {
+      qreg[2 * j] = *(const bf16x8*)(qh + 64 * (qj0 + j));
+      qreg[2 * j + 1] = *(const bf16x8*)(qh + 64 * (qj0 + j) + 8);
     }
     if constexpr (kRope) {
-      qrope[0] = *(const bf16x8*)(qh + 512);
-      qrope[1] = *(const bf16x8*)(qh + 512 + 8);
+#pragma unroll
+      for (int r = 0; r < NQR; ++r) qrope[r] = *(const bf16x8*)(qh + 512 + 8 * (qr0 + r));
     }
   };
   load_q(its[0].t);
 
-  f32x4 O[8];
+  f32x4 O[8 * NDG];  // dims 128 (NDG sub + dg) + 16 db + li of heads h0 + 4G + 0..3
   float m = kNegInf, l = 0.f;
   auto reset_state = [&]() {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 8 * NDG; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     m = kNegInf;
     l = 0.f;
   };
@@ -207,36 +234,37 @@ void decode_ring_kernel(DecodeParams p) {
     if (whole) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)(h0 + 4 * G + r) * p.o_sh + 128 * wr + li;
+        uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)(h0 + 4 * G + r) * p.o_sh + 128 * NDG * sub + li;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) orow[16 * db] = f32_to_bf16_bits(O[db][r] * ir[r]);
+        for (int db = 0; db < 8 * NDG; ++db) orow[16 * db] = f32_to_bf16_bits(O[db][r] * ir[r]);
       }
-      if (wr == 0 && G == 0) p.lse[(int64_t)t * p.l_st + h] = lse_out;
+      if (sub == 0 && G == 0) p.lse[(int64_t)t * p.l_st + h] = lse_out;
     } else {
       const int s = s_first + split_k;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float* orow = p.o_acc + ((int64_t)s * p.H + h0 + 4 * G + r) * kDv + 128 * wr + li;
+        float* orow = p.o_acc + ((int64_t)s * p.H + h0 + 4 * G + r) * kDv + 128 * NDG * sub + li;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) orow[16 * db] = O[db][r] * ir[r];
+        for (int db = 0; db < 8 * NDG; ++db) orow[16 * db] = O[db][r] * ir[r];
       }
-      if (wr == 0 && G == 0) p.lse_acc[(int64_t)s * p.H + h] = lse_out;
+      if (sub == 0 && G == 0) p.lse_acc[(int64_t)s * p.H + h] = lse_out;
     }
   };
 
-  // per-lane LDS byte offsets within a ring buffer
-  const uint32_t qk_off = (uint32_t)((16 * wr + li) * RS + 16 * G);         // + 64 j: dims 64j + 16G ..
-  const uint32_t sc_off = (uint32_t)((16 * wr + 4 * G) * RS + 512);         // + r RS: scales of row 16wr+4G+r
-  const uint32_t pv_off = (uint32_t)((8 * G + (li >> 1)) * RS + 128 * wr + 8 * (li & 1));  // + 32 kk RS + 16 db
-  const uint32_t vs_off = (uint32_t)(lane * RS + 512 + 4 * wr);             // scale of group wr of row `lane`
+  // per-lane LDS byte offsets within a ring buffer; this wave's QK^T rows are the 16-row blocks
+  // NRB sub + rb, its PV dims the 128-dim groups NDG sub + dg
+  const uint32_t qk_off = (uint32_t)(li * RS + 16 * G);       // + 16 blk RS + 64 j: dims 64j + 16G ..
+  const uint32_t sc_off = (uint32_t)(4 * G * RS + 512);       // + 16 blk RS + r RS: scales of row 4G + r
+  const uint32_t pv_off = (uint32_t)((8 * G + (li >> 1)) * RS + 128 * NDG * sub + 8 * (li & 1));  // + 32 kk RS + 16 db
+  const uint32_t vs_off = (uint32_t)(lane * RS + 512 + 4 * NDG * sub);      // + 4 dg: scale of group NDG sub + dg
 
   // Global operations this wave certainly issued after each gather, for the wait on that gather: the
   // Q loads that follow the gather in its iteration (cnt_tail), and everything of each later
   // iteration (cnt_iter: output stores, the next gather, Q loads). Slot id loads are not counted
   // (a load whose lanes are all masked may be skipped), nor the slot-scale load of a gather, so the
   // counts are lower bounds and the wait never returns early.
-  constexpr int QN = kRope ? 18 : 16;  // 16-byte Q loads
-  constexpr int SN = 32;               // output stores of an epilogue (per lane: 4 heads x 8 dim blocks)
+  constexpr int QN = 2 * NQJ + (kRope ? NQR : 0);  // 16-byte Q loads
+  constexpr int SN = 32 * NDG;         // output stores of an epilogue (per lane: 4 heads x 8 NDG dim blocks)
   // Entry r of these describes iteration k-NB+1+r (r = 0: the iteration that issued tile k's gather;
   // the prologue counts as iterations -NB+1 .. -1, issuing the gathers of tiles 0 .. NB-2 and then Q).
   int cnt_tail[NB - 1], cnt_iter[NB - 1];
@@ -282,61 +310,72 @@ void decode_ring_kernel(DecodeParams p) {
     const Item it0 = its[0], it1 = its[1];
     const ListDev& ld = LD(it0.L);
     const bool slot_scaled = ld.format == SDA_FP8_SLOTSCALE;
-    const uint32_t vmw = HS == 1 ? sm.vmask[b][wr] : (sm.vmask[b][2 * wr] | (sm.vmask[b][2 * wr + 1] << 8));
     uint32_t vany = 0;
 #pragma unroll
-    for (int j = 0; j < 4 * HS; ++j) vany |= sm.vmask[b][j];
+    for (int j = 0; j < Shape::NW; ++j) vany |= sm.vmask[b][j];
     const bool any = vany != 0;
     const char* ring = sm.ring[b];
 
     if (any) {
-      // ---- QK^T for rows 16wr .. 16wr+15
-      f32x4 acc[4];
-      f32x4 accr = f32x4{0.f, 0.f, 0.f, 0.f};
+      // ---- QK^T for the wave's 16-row blocks (over its 128-dim groups g0 .. g0 + QG - 1)
+      constexpr int QRB = kDimSplit ? 4 : NRB;
+      constexpr int QG = kDimSplit ? 2 : 4;
+      const int g0 = kDimSplit ? 2 * sub : 0;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < QRB; ++rb) {
+        const int blk = kDimSplit ? rb : NRB * sub + rb;  // rows 16 blk .. 16 blk + 15
+        // valid rows of the block: gathered by one wave (16 rows each) or two (8 rows each)
+        const uint32_t vmw = RW == 16 ? sm.vmask[b][blk] : (sm.vmask[b][2 * blk] | (sm.vmask[b][2 * blk + 1] << 8));
+        const uint32_t blk_off = (uint32_t)(16 * blk * RS);
+        f32x4 acc[QG];
+        f32x4 accr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 lo[4], hi[4];
+        for (int g = 0; g < QG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x4 x = *(const u32x4*)(ring + qk_off + 64 * (2 * g + half));
-          e4m3x16_to_bf16(x, lo[g], hi[g]);
+        for (int half = 0; half < 2; ++half) {
+          u32x4 x[QG];
+#pragma unroll
+          for (int g = 0; g < QG; ++g) x[g] = *(const u32x4*)(ring + qk_off + blk_off + 64 * (2 * (g0 + g) + half));
+          // each fragment is widened right before its two products (short-lived temporaries)
+#pragma unroll
+          for (int g = 0; g < QG; ++g) {
+            bf16x8 lo, hi;
+            e4m3x16_to_bf16(x[g], lo, hi);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qreg[2 * (2 * g + half)], acc[g], 0, 0, 0);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qreg[2 * (2 * g + half) + 1], acc[g], 0, 0, 0);
+          }
         }
+        if constexpr (kRope) {
+          const char* rr = ring + (16 * blk + li) * RS + 528 + 32 * G + 16 * qr0;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g], qreg[2 * (2 * g + half)], acc[g], 0, 0, 0);
+          for (int r = 0; r < NQR; ++r)
+            accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(rr + 16 * r), qrope[r], accr, 0, 0, 0);
+        }
+        // fold the rows' scales, mask, write the (partial) scores
+        f32x4 sc[4];
+        if (slot_scaled) {
+          const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * blk + 4 * G];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[g], qreg[2 * (2 * g + half) + 1], acc[g], 0, 0, 0);
+          for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[r] = *(const f32x4*)(ring + sc_off + blk_off + r * RS);
+        }
+        f32x4 s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = accr[r];
+#pragma unroll
+          for (int g = 0; g < QG; ++g) v += acc[g][r] * sc[r][g0 + g];
+          s[r] = ((vmw >> (4 * G + r)) & 1u) ? v * p.scale_log2 : kNegInf;
+        }
+        sm.sx[kDimSplit ? sub : 0][hs][blk][lane] = s;
       }
-      if constexpr (kRope) {
-        const bf16x8 r0 = *(const bf16x8*)(ring + (16 * wr + li) * RS + 528 + 32 * G);
-        const bf16x8 r1 = *(const bf16x8*)(ring + (16 * wr + li) * RS + 528 + 32 * G + 16);
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0, qrope[0], accr, 0, 0, 0);
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1, qrope[1], accr, 0, 0, 0);
+      // the scale of each of this wave's dim groups for every row (PV of all head sets)
+      if (hs == 0 && !slot_scaled) {
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) sm.vs[NDG * sub + dg][lane] = *(const float*)(ring + vs_off + 4 * dg);
       }
-      // fold the rows' scales, mask, write the scores
-      f32x4 sc[4];
-      if (slot_scaled) {
-        const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * wr + 4 * G];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = *(const f32x4*)(ring + sc_off + r * RS);
-      }
-      f32x4 s;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = accr[r];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) v += acc[g][r] * sc[r][g];
-        s[r] = ((vmw >> (4 * G + r)) & 1u) ? v * p.scale_log2 : kNegInf;
-      }
-      sm.sx[hs][wr][lane] = s;
-      // the scale of dim group wr for every row (PV of both head sets)
-      if (hs == 0 && !slot_scaled) sm.vs[wr][lane] = *(const float*)(ring + vs_off);
     }
     barrier_lds();  // scores of all rows visible
 
@@ -355,8 +394,12 @@ void decode_ring_kernel(DecodeParams p) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int wv = 2 * kk + (G >> 1);
-          const f32x4 a = sm.sx[hs][wv][16 * (2 * (G & 1)) + li];
-          const f32x4 c = sm.sx[hs][wv][16 * (2 * (G & 1) + 1) + li];
+          f32x4 a = sm.sx[0][hs][wv][16 * (2 * (G & 1)) + li];
+          f32x4 c = sm.sx[0][hs][wv][16 * (2 * (G & 1) + 1) + li];
+          if constexpr (kDimSplit) {  // the other half's partial scores (a masked row is -inf in both)
+            a += sm.sx[1][hs][wv][16 * (2 * (G & 1)) + li];
+            c += sm.sx[1][hs][wv][16 * (2 * (G & 1) + 1) + li];
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             z[kk][r] = a[r];
@@ -389,69 +432,66 @@ void decode_ring_kernel(DecodeParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * G + r);
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
+          for (int db = 0; db < 8 * NDG; ++db) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) O[db][r] *= ar[r];
           }
         }
       }
 
-      // ---- P' = p x scale (this wave's dim group), split into bf16 terms
-      bf16x8 A[2][NTERM];
-      {
-        const float* vsrc = slot_scaled ? sm.sscale[b] : sm.vs[wr];
+      // ---- per dim group of this wave: P' = p x the rows' scale of the group, split into bf16 terms;
+      // O += P' V over its 128 dims in two halves of 4 dim blocks (the transposed reads of the second
+      // half are in flight during the products of the first)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const f32x4 a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
-          const f32x4 c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
-          float pg[8];
+      for (int dg = 0; dg < NDG; ++dg) {
+        bf16x8 A[2][NTERM];
+        {
+          const float* vsrc = slot_scaled ? sm.sscale[b] : sm.vs[NDG * sub + dg];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pg[r] = pv[kk][r] * a[r];
-            pg[4 + r] = pv[kk][4 + r] * c[r];
+          for (int kk = 0; kk < 2; ++kk) {
+            const f32x4 a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
+            const f32x4 c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
+            float pg[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pg[r] = pv[kk][r] * a[r];
+              pg[4 + r] = pv[kk][4 + r] * c[r];
+            }
+            split_terms<NTERM>(pg, A[kk]);
           }
-          split_terms<NTERM>(pg, A[kk]);
         }
+        const uint32_t vaddr = lds_u32(ring) + pv_off + 128 * dg;
+        i32x2 x[2][4][2];
+        auto read_half = [&](int half) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) x[half][d][kk] = lds_tr8(vaddr + 32 * kk * RS + 16 * (4 * half + d));
+          }
+        };
+        auto mma_half = [&](int half) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const bf16x8 B = e4m3x8_to_bf16(x[half][d][kk]);
+              f32x4& o = O[8 * dg + 4 * half + d];
+#pragma unroll
+              for (int t = 0; t < NTERM; ++t) o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk][t], B, o, 0, 0, 0);
+            }
+          }
+        };
+        read_half(0);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(x[0][0][0]), "+v"(x[0][0][1]), "+v"(x[0][1][0]), "+v"(x[0][1][1]), "+v"(x[0][2][0]),
+                       "+v"(x[0][2][1]), "+v"(x[0][3][0]), "+v"(x[0][3][1]));
+        read_half(1);
+        mma_half(0);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(x[1][0][0]), "+v"(x[1][0][1]), "+v"(x[1][1][0]), "+v"(x[1][1][1]), "+v"(x[1][2][0]),
+                       "+v"(x[1][2][1]), "+v"(x[1][3][0]), "+v"(x[1][3][1]));
+        mma_half(1);
       }
-
-      // ---- O += P' V over dims 128wr .. 128wr+127, in two halves of 4 dim blocks; the transposed
-      // reads of the second half are in flight during the products of the first
-      const uint32_t vaddr = lds_u32(ring) + pv_off;
-      i32x2 x[2][4][2];
-      auto read_half = [&](int half) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) x[half][d][kk] = lds_tr8(vaddr + 32 * kk * RS + 16 * (4 * half + d));
-        }
-      };
-      auto mma_half = [&](int half) {
-        bf16x8 B[4][2];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) B[d][kk] = e4m3x8_to_bf16(x[half][d][kk]);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int t = 0; t < NTERM; ++t) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              O[4 * half + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk][t], B[d][kk], O[4 * half + d], 0, 0, 0);
-          }
-        }
-      };
-      read_half(0);
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(x[0][0][0]), "+v"(x[0][0][1]), "+v"(x[0][1][0]), "+v"(x[0][1][1]), "+v"(x[0][2][0]),
-                     "+v"(x[0][2][1]), "+v"(x[0][3][0]), "+v"(x[0][3][1]));
-      read_half(1);
-      mma_half(0);
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(x[1][0][0]), "+v"(x[1][0][1]), "+v"(x[1][1][0]), "+v"(x[1][1][1]), "+v"(x[1][2][0]),
-                     "+v"(x[1][2][1]), "+v"(x[1][3][0]), "+v"(x[1][3][1]));
-      mma_half(1);
     }
 
     if (it1.end() || it1.t != it0.t) {
@@ -478,24 +518,29 @@ void decode_ring_kernel(DecodeParams p) {
 template <int DQK, int HS, int NB>
 static hipError_t launch_ring_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * HS));
+  const dim3 block(64 * RingShape<HS>::NW);
   if (precision == 1)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB>), grid, block, 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB>), grid, dim3(256 * HS), 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-// 16 heads per workgroup: two workgroups per CU, two ring buffers each. 32 heads per workgroup (eight
-// waves, one workgroup per CU): three ring buffers.
+// 16 heads per workgroup: two workgroups per CU, two ring buffers each. 32 heads (eight waves, one
+// workgroup per CU): three ring buffers. 64 heads (eight waves with twice the rows and dims each):
+// three ring buffers, every record gathered once per 64 heads.
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream) {
-  if (d_qk == 576)
-    return heads_per_group == 16 ? launch_ring_t<576, 1, 2>(p, num_parts, precision, stream)
-                                 : launch_ring_t<576, 2, 3>(p, num_parts, precision, stream);
-  return heads_per_group == 16 ? launch_ring_t<512, 1, 2>(p, num_parts, precision, stream)
-                               : launch_ring_t<512, 2, 3>(p, num_parts, precision, stream);
+  if (d_qk == 576) {
+    if (heads_per_group == 16) return launch_ring_t<576, 1, 2>(p, num_parts, precision, stream);
+    if (heads_per_group == 32) return launch_ring_t<576, 2, 3>(p, num_parts, precision, stream);
+    return launch_ring_t<576, 4, 3>(p, num_parts, precision, stream);
+  }
+  if (heads_per_group == 16) return launch_ring_t<512, 1, 2>(p, num_parts, precision, stream);
+  if (heads_per_group == 32) return launch_ring_t<512, 2, 3>(p, num_parts, precision, stream);
+  return launch_ring_t<512, 4, 3>(p, num_parts, precision, stream);
 }
 
 }  // namespace sda

@@ -69,6 +69,21 @@ def test_any_plan_same_result(parts, hb, F):
     compare(out, lse, o_ref, l_ref, what=f"plan {parts}/{hb}/{F}")
 
 
+# 64-head workgroups (eight waves with 32 rows and 256 dims each) for every fp8 record layout; a call
+# with an NVFP4 list runs 32-head workgroups under the same plan
+@pytest.mark.parametrize("fmt,xfmt,H", [(wl.FP8_SLOTSCALE, None, 64), (wl.FP8_528, wl.FP8_528, 128),
+                                        (wl.V32_656, None, 64), (wl.V32_656, None, 128),
+                                        (wl.FP8_528, wl.NVFP4_288, 64)])
+@pytest.mark.parametrize("parts", [5, 40])
+def test_64_head_workgroups(fmt, xfmt, H, parts):
+    w = wl.small_workload(70 + fmt + parts, fmt, xfmt, T=7, H=H, width=150, xwidth=260 if xfmt is not None else 0,
+                          num_slots=2048, sink=True, p_invalid=0.05, lens_lo=0)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    dw = DeviceWorkload(w)
+    out, lse, dec = dw.run(plan=sda.sda_plan(parts, 64, 2, 2))
+    compare(out, lse, o_ref, l_ref, what=f"64-head plan, {parts} parts", count_flips=True)
+
+
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
 @pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
 def test_heads_and_formats(H, fmt):
