@@ -48,6 +48,8 @@ def lib():
         L.orc_e4m3.argtypes = [ctypes.c_int]
         L.orc_e2m1.restype = ctypes.c_double
         L.orc_e2m1.argtypes = [ctypes.c_int]
+        L.orc_ue8m0.restype = ctypes.c_double
+        L.orc_ue8m0.argtypes = [ctypes.c_int]
         L.orc_bf16.restype = ctypes.c_double
         L.orc_bf16.argtypes = [ctypes.c_int]
         L.orc_record_bytes.argtypes = [ctypes.c_int]

@@ -37,6 +37,14 @@ double orc_e2m1(int nibble) {
   return s ? -v : v;
 }
 
+/* ue8m0 (OCP MX scale, "E8M0"): an unsigned biased exponent, 2^(byte - 127),
+ * no sign and no mantissa; 0xFF is NaN. */
+double orc_ue8m0(int byte) {
+  byte &= 0xFF;
+  if (byte == 0xFF) return NAN;
+  return ldexp(1.0, byte - 127);
+}
+
 /* bf16 is the upper half of an IEEE binary32 word. */
 double orc_bf16(int bits) {
   uint32_t u = ((uint32_t)bits & 0xFFFFu) << 16;
@@ -58,6 +66,7 @@ int orc_record_bytes(int format) {
     case ORC_FP8_528: return 512 + 4 * 4;       /* codes, then one fp32 per 128 dims       */
     case ORC_NVFP4_288: return 256 + 32;        /* packed e2m1, then one e4m3 per 16 dims  */
     case ORC_V32_656: return 512 + 4 * 4 + 64 * 2; /* codes, 4 fp32 scales, 64 bf16 dims   */
+    case ORC_FP8_UE8M0: return 512 + 16;        /* codes, then one ue8m0 per 32 dims       */
     default: return -1;
   }
 }
@@ -66,7 +75,8 @@ int orc_record_dims(int format) {
   switch (format) {
     case ORC_FP8_SLOTSCALE:
     case ORC_FP8_528:
-    case ORC_NVFP4_288: return 512;
+    case ORC_NVFP4_288:
+    case ORC_FP8_UE8M0: return 512;
     case ORC_V32_656: return 576;
     default: return -1;
   }
@@ -94,6 +104,13 @@ int orc_decode_slot(const orc_cache* c, int64_t sid, double* k) {
       for (d = 0; d < 512; d++) k[d] = orc_e4m3(r[d]) * f32_le(r + 512 + 4 * (d / 128));
       if (c->format == ORC_V32_656)
         for (d = 0; d < 64; d++) k[512 + d] = orc_bf16(r[528 + 2 * d] | (r[528 + 2 * d + 1] << 8));
+      break;
+    }
+    case ORC_FP8_UE8M0: {
+      /* vLLM swapab_decode_attn page, stage_inputs (fp8 branch): 16-byte chunk c
+       * holds dims 16c..16c+15 and takes scale byte c / 2, i.e. scale byte g
+       * covers dims 32g..32g+31 */
+      for (d = 0; d < 512; d++) k[d] = orc_e4m3(r[d]) * orc_ue8m0(r[512 + d / 32]);
       break;
     }
     case ORC_NVFP4_288: {

@@ -64,6 +64,11 @@ def decode_rows(cache, sids) -> np.ndarray:
             if cache.fmt == 3:
                 row = np.concatenate([row, bf16_torch(r[528:656].copy().view(np.uint16))])
             out.append(row)
+        elif cache.fmt == 4:  # FP8_UE8M0
+            g = L["fp8_ue8m0_528"]["scale_group_dims"]
+            e = r[512:528].astype(np.float64)
+            sc = np.where(e == 255, np.nan, np.exp2(e - 127.0))
+            out.append(e4m3_torch(r[:512]) * np.repeat(sc, g))
         elif cache.fmt == 2:  # NVFP4_288
             packed = r[:256]
             nib = np.empty(512, dtype=np.int64)

@@ -53,12 +53,14 @@ def test_record_sizes_match_pages(orc):
     assert L.orc_record_bytes(wl.FP8_528) == g["fp8_528"]["bytes"] == sum(g["fp8_528"]["parts"].values())
     assert L.orc_record_bytes(wl.NVFP4_288) == g["nvfp4_288"]["bytes"] == sum(g["nvfp4_288"]["parts"].values())
     assert L.orc_record_bytes(wl.FP8_SLOTSCALE) == g["fp8_slotscale_512"]["bytes"]
+    assert L.orc_record_bytes(wl.FP8_UE8M0) == g["fp8_ue8m0_528"]["bytes"] == sum(g["fp8_ue8m0_528"]["parts"].values())
+    assert L.orc_record_dims(wl.FP8_UE8M0) == 512
     assert L.orc_record_dims(wl.V32_656) == 576 and L.orc_record_dims(wl.FP8_528) == 512
     for f in wl.RECORD_BYTES:
         assert L.orc_record_bytes(f) == wl.RECORD_BYTES[f]
 
 
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0])
 @pytest.mark.parametrize("pad", [0, 96])
 def test_decode_slot_matches_library_decoding(orc, fmt, pad):
     rng = np.random.default_rng(fmt * 10 + pad)
@@ -86,6 +88,48 @@ def test_nvfp4_chunk_and_scale_mapping(orc):
     rec[0] = 0x67                         # low nibble (7 = 6.0) -> element 0, high (6 = 4.0) -> element 1
     k = orc.decode_slot(c, 0)
     assert k[0] == 6.0 * sc[0] and k[1] == 4.0 * sc[0]
+
+
+def test_ue8m0_values(orc):
+    """ue8m0 (OCP MX scale): 2^(byte - 127), 0xFF NaN."""
+    L = orc.lib()
+    assert L.orc_ue8m0(127) == 1.0 and L.orc_ue8m0(130) == 8.0 and L.orc_ue8m0(124) == 0.125
+    assert L.orc_ue8m0(0) == 2.0 ** -127 and L.orc_ue8m0(254) == 2.0 ** 127
+    assert np.isnan(L.orc_ue8m0(255))
+
+
+def test_ue8m0_chunk_and_scale_mapping(orc):
+    """Scale byte g covers dims [32g, 32g+32) (chunk c of 16 dims takes byte c // 2, vLLM page)."""
+    c = wl.make_cache(np.random.default_rng(0), wl.FP8_UE8M0, 64, page_size=64)
+    rec = c.data[:528]
+    rec[:512] = 0x38                                      # e4m3 1.0 in every dim
+    rec[512:528] = 119 + np.arange(16, dtype=np.uint8)    # scales 2^-8 .. 2^7
+    k = orc.decode_slot(c, 0)
+    assert np.array_equal(k, np.repeat(2.0 ** (np.arange(16) - 8), 32))
+    rec[16:32] = 0x40                                     # chunk 1 (dims 16..31): e4m3 2.0, still scale byte 0
+    rec[32:48] = 0xB8                                     # chunk 2 (dims 32..47): e4m3 -1.0, scale byte 1
+    k = orc.decode_slot(c, 0)
+    assert np.all(k[16:32] == 2.0 * 2.0 ** -8) and np.all(k[32:48] == -(2.0 ** -7))
+
+
+def test_ue8m0_equals_fp32_scales_when_a_group_shares_one(orc):
+    """A record whose four scale bytes of each 128-dim group are equal decodes, and attends, exactly like
+    the FP8_528 record with those powers of two as its fp32 group scales."""
+    w = _w(21, fmt=wl.FP8_UE8M0)
+    c = w.cache
+    n = c.num_slots
+    recs = c.data.reshape(c.num_pages, c.page_stride)[:, : c.page_size * 528].reshape(n, 528)
+    recs[:, 512:528] = np.repeat(recs[:, 512:528:4], 4, axis=1)    # one exponent per 128 dims
+    w2 = copy.deepcopy(w)
+    c2 = w2.cache
+    c2.fmt = wl.FP8_528
+    r2 = c2.data.reshape(c2.num_pages, c2.page_stride)[:, : c2.page_size * 528].reshape(n, 528)
+    r2[:, 512:528] = np.exp2(recs[:, 512:528:4].astype(np.float64) - 127).astype(np.float32).view(np.uint8).reshape(n, 16)
+    for s in (0, 5, n - 1):
+        assert np.array_equal(orc.decode_slot(c, s), orc.decode_slot(c2, s))
+    o1, l1 = orc.attention(w)
+    o2, l2 = orc.attention(w2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_slot_range_masking(orc):
@@ -237,7 +281,7 @@ def test_lens_zero_gives_zero_output_and_sink_lse(orc):
     assert np.all(out == 0) and np.all(lse == -np.inf)
 
 
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0])
 def test_single_valid_slot_returns_its_row(orc, fmt):
     w = _w(6, fmt=fmt, width=8)
     w.lst.idx[:, :] = -1

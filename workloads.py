@@ -18,9 +18,15 @@ Record formats (bytes of one slot; ``page_stride`` bytes between pages):
 * ``V32_656`` (656 B): 512 e4m3 codes, 4 fp32 scales (per 128 dims), then 64
   bf16 values for dims 512..575 (FlashMLA sparse_decode.h page: the V3.2
   bytes-per-token sum 512 + 64*2 + 4*4).
+* ``FP8_UE8M0`` (528 B): 512 e4m3 codes, then 16 ue8m0 scale bytes, byte g the
+  power-of-two scale 2^(g - 127) of dims 32g..32g+31 (vLLM swapab_decode_attn
+  page, stage_inputs: fp8 chunk c of 16 dims takes scale byte c // 2).
 
 Quantization of the synthetic N(0,1) data: e4m3 by torch's float8_e4m3fn cast
-after clipping to +-448 (round-to-nearest-even with saturation); NVFP4 by the
+after clipping to +-448 (round-to-nearest-even with saturation); FP8_UE8M0 rows
+first get a random magnitude 2^U{-4..4} per 32-dim block, then each block the
+scale exponent ceil(log2(amax / 448)) (the MXFP8 rule of the vLLM page's output
+cast) and codes e4m3(x / scale); NVFP4 by the
 usual recipe, block scale = e4m3(amax/6) and codes = round-to-nearest-even of
 x/scale on the e2m1 grid, saturating at 6 (torch has no float->e2m1 cast, so
 the grid rounding is written out here).
@@ -34,10 +40,11 @@ from typing import Optional
 import numpy as np
 import torch
 
-FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656 = 0, 1, 2, 3
-FORMAT_NAMES = {FP8_SLOTSCALE: "fp8_slotscale", FP8_528: "fp8_528", NVFP4_288: "nvfp4_288", V32_656: "v32_656"}
-RECORD_BYTES = {FP8_SLOTSCALE: 512, FP8_528: 528, NVFP4_288: 288, V32_656: 656}
-D_QK = {FP8_SLOTSCALE: 512, FP8_528: 512, NVFP4_288: 512, V32_656: 576}
+FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656, FP8_UE8M0 = 0, 1, 2, 3, 4
+FORMAT_NAMES = {FP8_SLOTSCALE: "fp8_slotscale", FP8_528: "fp8_528", NVFP4_288: "nvfp4_288", V32_656: "v32_656",
+                FP8_UE8M0: "fp8_ue8m0"}
+RECORD_BYTES = {FP8_SLOTSCALE: 512, FP8_528: 528, NVFP4_288: 288, V32_656: 656, FP8_UE8M0: 528}
+D_QK = {FP8_SLOTSCALE: 512, FP8_528: 512, NVFP4_288: 512, V32_656: 576, FP8_UE8M0: 512}
 
 
 @dataclasses.dataclass
@@ -107,6 +114,19 @@ def e4m3_codes(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def ue8m0_records(rng: np.random.Generator, x: np.ndarray) -> np.ndarray:
+    """[n, 512] float32 -> [n, 528] FP8_UE8M0 records: per 32-dim block a random magnitude 2^U{-4..4}, then
+    the block's scale byte 127 + ceil(log2(amax / 448)) (clamped to 1..254) and codes e4m3(x / scale)."""
+    n = x.shape[0]
+    blocks = x.reshape(n, 16, 32) * np.exp2(rng.integers(-4, 5, size=(n, 16, 1))).astype(np.float32)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.ceil(np.log2(amax / 448.0)), -127.0)
+    ex = np.clip(ex, -126, 127).astype(np.int32)
+    codes = e4m3_codes((blocks / np.exp2(ex)[:, :, None].astype(np.float32)).reshape(n, 512))
+    return np.concatenate([codes, (ex + 127).astype(np.uint8)], axis=1)
+
+
 def e4m3_values(codes: np.ndarray) -> np.ndarray:
     """e4m3fn codes -> float32 via torch's cast (used only to build NVFP4 block scales)."""
     return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float32).numpy()
@@ -162,6 +182,9 @@ def make_cache(rng: np.random.Generator, fmt: int, num_slots: int, page_size: in
         x = rng.standard_normal((n, 512), dtype=np.float32)
         if fmt == NVFP4_288:
             recs[s0:s0 + n] = nvfp4_records(x)
+            continue
+        if fmt == FP8_UE8M0:
+            recs[s0:s0 + n] = ue8m0_records(rng, x)
             continue
         recs[s0:s0 + n, :512] = e4m3_codes(x)
         if fmt in (FP8_528, V32_656):
