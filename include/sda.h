@@ -62,8 +62,12 @@ enum sda_status {
  *                    [16b, 16b+16) (vLLM swapab_decode_attn, stage_inputs, NVFP4 branch).
  * SDA_V32_656        656 B: as SDA_FP8_528 for dims 0..511, then 64 little-endian bf16 values for
  *                    dims 512..575 (FlashMLA sparse_decode.h: V3.2 bytes_per_token); d_qk = 576.
- * A decoded value is code * scale (exact in bf16 for every format). */
-enum sda_format { SDA_FP8_SLOTSCALE = 0, SDA_FP8_528 = 1, SDA_NVFP4_288 = 2, SDA_V32_656 = 3 };
+ * SDA_FP8_UE8M0      528 B: 512 e4m3fn codes, then 16 ue8m0 scale bytes, byte g the power of two
+ *                    2^(g - 127) covering dims [32g, 32g+32) (vLLM swapab_decode_attn, stage_inputs,
+ *                    fp8 branch); byte 255 (NaN in the MX encoding) gives NaN rows.
+ * A decoded value is code * scale (exact in bf16 for every format; for SDA_FP8_UE8M0 while it stays
+ * within the bf16 range). */
+enum sda_format { SDA_FP8_SLOTSCALE = 0, SDA_FP8_528 = 1, SDA_NVFP4_288 = 2, SDA_V32_656 = 3, SDA_FP8_UE8M0 = 4 };
 
 /* A paged cache. Slot id s lives in page s / page_size at offset s % page_size; its record starts
  * at base + (s / page_size) * page_stride + (s % page_size) * record_bytes. Pages may be further

@@ -131,9 +131,13 @@ namespace sda {
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream) {
   const bool fp4 = p.lst[0].format == SDA_NVFP4_288 || (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288);
+  // the ring kernel takes FP8_UE8M0 lists only when every list is one
+  const int ue = (p.lst[0].format == SDA_FP8_UE8M0) + (p.nlists > 1 && p.lst[1].format == SDA_FP8_UE8M0);
+  const bool staged = fp4 || (ue > 0 && ue < p.nlists);
   // the register-staged kernel takes at most 32 heads per workgroup
-  return fp4 ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision, stream)
-             : launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
+  return staged ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision,
+                                       stream)
+                : launch_decode_ring(p, num_parts, heads_per_group, d_qk, precision, stream);
 }
 }  // namespace sda
 
@@ -182,6 +186,7 @@ int sda_record_bytes(int format) {
     case SDA_FP8_528: return 528;
     case SDA_NVFP4_288: return 288;
     case SDA_V32_656: return 656;
+    case SDA_FP8_UE8M0: return 528;
     default: return -1;
   }
 }
@@ -190,7 +195,8 @@ int sda_format_dims(int format) {
   switch (format) {
     case SDA_FP8_SLOTSCALE:
     case SDA_FP8_528:
-    case SDA_NVFP4_288: return 512;
+    case SDA_NVFP4_288:
+    case SDA_FP8_UE8M0: return 512;
     case SDA_V32_656: return 576;
     default: return -1;
   }

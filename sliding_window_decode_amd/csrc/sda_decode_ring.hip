@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sda_device.h"
 #include "sda_internal.h"
 #include "sda_items.h"
@@ -58,25 +60,29 @@ struct RingShape {
   static constexpr int NPART = kDimSplit ? 2 : 1;  // partial score arrays
 };
 
-template <int DQK, int HS, int NB>
+template <int DQK, int HS, int NB, bool UE>
 struct RingSmem {
   static constexpr int RS = DQK == 576 ? 656 : 528;  // ring row stride in bytes (odd number of chunks)
   static constexpr int NW = RingShape<HS>::NW;
   char ring[NB][kTileRows * RS];
   f32x4 sx[RingShape<HS>::NPART][HS][4][64];  // (partial) scores per 16-row block and head set, MFMA layout
   float sscale[NB][64];         // per-slot scales (FP8_SLOTSCALE)
-  float vs[4][64];              // per dim group: its scale for every row of the tile
+  // per scale group: its scale for every row of the tile (128-dim groups; the ue8m0 format's 32-dim
+  // groups in the kernels built for it)
+  float vs[UE ? 16 : 4][64];
   uint32_t vmask[NB][NW];       // valid rows of each ring buffer, one mask per gathering wave
   uint64_t raddr[NW][RingShape<HS>::RW];  // per wave: record addresses of the rows it gathers
 };
 
 // HS head sets of 16 heads per workgroup (HS = 1, 2, 4: 16, 32 or 64 heads), NB ring buffers (tiles
-// k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'.
-template <int DQK, int HS, int NTERM, int NB>
+// k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'. UE: built for calls whose
+// lists are all FP8_UE8M0 (512 dims), and only for them (carrying both decodings raises the register
+// pressure of every call; calls that mix it with another format run the staged kernel).
+template <int DQK, int HS, int NTERM, int NB, bool UE>
 __global__ __launch_bounds__(64 * RingShape<HS>::NW)
 __attribute__((amdgpu_waves_per_eu(RingShape<HS>::NW == 8 || (DQK == 512 && NB == 2) ? 2 : 1)))
 void decode_ring_kernel(DecodeParams p) {
-  using Smem = RingSmem<DQK, HS, NB>;
+  using Smem = RingSmem<DQK, HS, NB, UE>;
   using Shape = RingShape<HS>;
   constexpr int RS = Smem::RS;
   constexpr int RSC = RS / 16;                // chunks per ring row
@@ -84,6 +90,7 @@ void decode_ring_kernel(DecodeParams p) {
   constexpr int NRB = Shape::NRB, NDG = Shape::NDG;
   constexpr int NI = (RW * RSC + 63) / 64;    // gather instructions per wave and tile
   constexpr bool kRope = DQK == 576;
+  constexpr bool kUe8m0 = UE && DQK == 512;  // FP8_UE8M0 records hold 512 dims
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -321,60 +328,85 @@ void decode_ring_kernel(DecodeParams p) {
       constexpr int QRB = kDimSplit ? 4 : NRB;
       constexpr int QG = kDimSplit ? 2 : 4;
       const int g0 = kDimSplit ? 2 * sub : 0;
+      // SCALED: FP8_UE8M0 records, whose power-of-two scale of each 32 dims is applied by the conversion
+      // (the fold below then multiplies by 1); other formats convert unscaled
+      auto qk_blocks = [&](auto ue_tag) {
+        constexpr bool SCALED = decltype(ue_tag)::value;
 #pragma unroll
-      for (int rb = 0; rb < QRB; ++rb) {
-        const int blk = kDimSplit ? rb : NRB * sub + rb;  // rows 16 blk .. 16 blk + 15
-        // valid rows of the block: gathered by one wave (16 rows each) or two (8 rows each)
-        const uint32_t vmw = RW == 16 ? sm.vmask[b][blk] : (sm.vmask[b][2 * blk] | (sm.vmask[b][2 * blk + 1] << 8));
-        const uint32_t blk_off = (uint32_t)(16 * blk * RS);
-        f32x4 acc[QG];
-        f32x4 accr = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < QRB; ++rb) {
+          const int blk = kDimSplit ? rb : NRB * sub + rb;  // rows 16 blk .. 16 blk + 15
+          // valid rows of the block: gathered by one wave (16 rows each) or two (8 rows each)
+          const uint32_t vmw = RW == 16 ? sm.vmask[b][blk] : (sm.vmask[b][2 * blk] | (sm.vmask[b][2 * blk + 1] << 8));
+          const uint32_t blk_off = (uint32_t)(16 * blk * RS);
+          u32x4 sb = u32x4{0u, 0u, 0u, 0u};  // the row's 16 ue8m0 bytes
+          if constexpr (SCALED) sb = *(const u32x4*)(ring + (16 * blk + li) * RS + 512);
+          f32x4 acc[QG];
+          f32x4 accr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < QG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int g = 0; g < QG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 x[QG];
+          for (int half = 0; half < 2; ++half) {
+            u32x4 x[QG];
 #pragma unroll
-          for (int g = 0; g < QG; ++g) x[g] = *(const u32x4*)(ring + qk_off + blk_off + 64 * (2 * (g0 + g) + half));
-          // each fragment is widened right before its two products (short-lived temporaries)
+            for (int g = 0; g < QG; ++g) x[g] = *(const u32x4*)(ring + qk_off + blk_off + 64 * (2 * (g0 + g) + half));
+            // each fragment is widened right before its two products (short-lived temporaries); its 16
+            // dims 64 (2 (g0+g) + half) + 16G .. lie in 32-dim group 4 (g0+g) + 2 half + G / 2
 #pragma unroll
-          for (int g = 0; g < QG; ++g) {
-            bf16x8 lo, hi;
-            e4m3x16_to_bf16(x[g], lo, hi);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qreg[2 * (2 * g + half)], acc[g], 0, 0, 0);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qreg[2 * (2 * g + half) + 1], acc[g], 0, 0, 0);
+            for (int g = 0; g < QG; ++g) {
+              const float cs = SCALED ? ue8m0_scale(sb[g0 + g] >> (8 * (2 * half + (G >> 1)))) : 1.0f;
+              bf16x8 lo, hi;
+              e4m3x16_to_bf16_scaled(x[g], cs, lo, hi);
+              acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qreg[2 * (2 * g + half)], acc[g], 0, 0, 0);
+              acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qreg[2 * (2 * g + half) + 1], acc[g], 0, 0, 0);
+            }
           }
+          if constexpr (kRope) {
+            const char* rr = ring + (16 * blk + li) * RS + 528 + 32 * G + 16 * qr0;
+#pragma unroll
+            for (int r = 0; r < NQR; ++r)
+              accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(rr + 16 * r), qrope[r], accr, 0, 0, 0);
+          }
+          // fold the rows' scales, mask, write the (partial) scores
+          f32x4 sc[4];
+          if (slot_scaled) {
+            const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * blk + 4 * G];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
+          } else if (SCALED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = f32x4{1.f, 1.f, 1.f, 1.f};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = *(const f32x4*)(ring + sc_off + blk_off + r * RS);
+          }
+          f32x4 s;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = accr[r];
+#pragma unroll
+            for (int g = 0; g < QG; ++g) v += acc[g][r] * sc[r][g0 + g];
+            s[r] = ((vmw >> (4 * G + r)) & 1u) ? v * p.scale_log2 : kNegInf;
+          }
+          sm.sx[kDimSplit ? sub : 0][hs][blk][lane] = s;
         }
-        if constexpr (kRope) {
-          const char* rr = ring + (16 * blk + li) * RS + 528 + 32 * G + 16 * qr0;
-#pragma unroll
-          for (int r = 0; r < NQR; ++r)
-            accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(rr + 16 * r), qrope[r], accr, 0, 0, 0);
-        }
-        // fold the rows' scales, mask, write the (partial) scores
-        f32x4 sc[4];
-        if (slot_scaled) {
-          const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * blk + 4 * G];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] = *(const f32x4*)(ring + sc_off + blk_off + r * RS);
-        }
-        f32x4 s;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = accr[r];
-#pragma unroll
-          for (int g = 0; g < QG; ++g) v += acc[g][r] * sc[r][g0 + g];
-          s[r] = ((vmw >> (4 * G + r)) & 1u) ? v * p.scale_log2 : kNegInf;
-        }
-        sm.sx[kDimSplit ? sub : 0][hs][blk][lane] = s;
-      }
+      };
+      if constexpr (kUe8m0)
+        qk_blocks(std::true_type{});
+      else
+        qk_blocks(std::false_type{});
       // the scale of each of this wave's dim groups for every row (PV of all head sets)
       if (hs == 0 && !slot_scaled) {
+        if constexpr (kUe8m0) {
 #pragma unroll
-        for (int dg = 0; dg < NDG; ++dg) sm.vs[NDG * sub + dg][lane] = *(const float*)(ring + vs_off + 4 * dg);
+          for (int dg = 0; dg < NDG; ++dg) {
+            const uint32_t wd = *(const uint32_t*)(ring + vs_off + 4 * dg);  // the group's 4 ue8m0 bytes
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) sm.vs[4 * (NDG * sub + dg) + sg][lane] = ue8m0_scale(wd >> (8 * sg));
+          }
+        } else {
+#pragma unroll
+          for (int dg = 0; dg < NDG; ++dg) sm.vs[NDG * sub + dg][lane] = *(const float*)(ring + vs_off + 4 * dg);
+        }
       }
     }
     barrier_lds();  // scores of all rows visible
@@ -441,26 +473,58 @@ void decode_ring_kernel(DecodeParams p) {
 
       // ---- per dim group of this wave: P' = p x the rows' scale of the group, split into bf16 terms;
       // O += P' V over its 128 dims in two halves of 4 dim blocks (the transposed reads of the second
-      // half are in flight during the products of the first)
+      // half are in flight during the products of the first). FP8_UE8M0: one P' per 32 dims, in four
+      // quarters of 2 dim blocks.
+      auto make_p = [&](const float* vsrc, bf16x8 (&A)[2][NTERM]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const f32x4 a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
+          const f32x4 c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
+          float pg[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pg[r] = pv[kk][r] * a[r];
+            pg[4 + r] = pv[kk][4 + r] * c[r];
+          }
+          split_terms<NTERM>(pg, A[kk]);
+        }
+      };
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
-        bf16x8 A[2][NTERM];
-        {
-          const float* vsrc = slot_scaled ? sm.sscale[b] : sm.vs[NDG * sub + dg];
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const f32x4 a = *(const f32x4*)(vsrc + 32 * kk + 8 * G);
-            const f32x4 c = *(const f32x4*)(vsrc + 32 * kk + 8 * G + 4);
-            float pg[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pg[r] = pv[kk][r] * a[r];
-              pg[4 + r] = pv[kk][4 + r] * c[r];
-            }
-            split_terms<NTERM>(pg, A[kk]);
-          }
-        }
         const uint32_t vaddr = lds_u32(ring) + pv_off + 128 * dg;
+        if constexpr (kUe8m0) {
+          i32x2 x[2][2][2];  // [buffer][dim block of the quarter][kk]
+          auto read_q = [&](int sg, int buf) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) x[buf][d][kk] = lds_tr8(vaddr + 32 * kk * RS + 16 * (2 * sg + d));
+            }
+          };
+          read_q(0, 0);
+#pragma unroll
+          for (int sg = 0; sg < 4; ++sg) {
+            const int buf = sg & 1;
+            bf16x8 A[2][NTERM];
+            make_p(sm.vs[4 * (NDG * sub + dg) + sg], A);
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(x[buf][0][0]), "+v"(x[buf][0][1]), "+v"(x[buf][1][0]), "+v"(x[buf][1][1]));
+            if (sg < 3) read_q(sg + 1, buf ^ 1);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+              for (int d = 0; d < 2; ++d) {
+                const bf16x8 B = e4m3x8_to_bf16(x[buf][d][kk]);
+                f32x4& o = O[8 * dg + 2 * sg + d];
+#pragma unroll
+                for (int t = 0; t < NTERM; ++t) o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk][t], B, o, 0, 0, 0);
+              }
+            }
+          }
+          continue;
+        }
+        bf16x8 A[2][NTERM];
+        make_p(slot_scaled ? sm.sscale[b] : sm.vs[NDG * sub + dg], A);
         i32x2 x[2][4][2];
         auto read_half = [&](int half) {
 #pragma unroll
@@ -515,17 +579,25 @@ void decode_ring_kernel(DecodeParams p) {
   if (ep_t >= 0) epilogue(ep_t, ep_s, ep_n);
 }
 
-template <int DQK, int HS, int NB>
+template <int DQK, int HS, int NB, bool UE>
 static hipError_t launch_ring_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * HS));
   const dim3 block(64 * RingShape<HS>::NW);
   if (precision == 1)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB, UE>), grid, block, 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB, UE>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB, UE>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+template <int DQK, int HS, int NB>
+static hipError_t launch_ring_any(const DecodeParams& p, int num_parts, int precision, bool ue, hipStream_t stream) {
+  if constexpr (DQK == 512) {
+    if (ue) return launch_ring_t<DQK, HS, NB, true>(p, num_parts, precision, stream);
+  }
+  return launch_ring_t<DQK, HS, NB, false>(p, num_parts, precision, stream);
 }
 
 // 16 heads per workgroup: two workgroups per CU, two ring buffers each. 32 heads (eight waves, one
@@ -533,14 +605,15 @@ static hipError_t launch_ring_t(const DecodeParams& p, int num_parts, int precis
 // three ring buffers, every record gathered once per 64 heads.
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream) {
+  const bool ue = p.lst[0].format == SDA_FP8_UE8M0;  // then every list is (launch_decode)
   if (d_qk == 576) {
-    if (heads_per_group == 16) return launch_ring_t<576, 1, 2>(p, num_parts, precision, stream);
-    if (heads_per_group == 32) return launch_ring_t<576, 2, 3>(p, num_parts, precision, stream);
-    return launch_ring_t<576, 4, 3>(p, num_parts, precision, stream);
+    if (heads_per_group == 16) return launch_ring_any<576, 1, 2>(p, num_parts, precision, false, stream);
+    if (heads_per_group == 32) return launch_ring_any<576, 2, 3>(p, num_parts, precision, false, stream);
+    return launch_ring_any<576, 4, 3>(p, num_parts, precision, false, stream);
   }
-  if (heads_per_group == 16) return launch_ring_t<512, 1, 2>(p, num_parts, precision, stream);
-  if (heads_per_group == 32) return launch_ring_t<512, 2, 3>(p, num_parts, precision, stream);
-  return launch_ring_t<512, 4, 3>(p, num_parts, precision, stream);
+  if (heads_per_group == 16) return launch_ring_any<512, 1, 2>(p, num_parts, precision, ue, stream);
+  if (heads_per_group == 32) return launch_ring_any<512, 2, 3>(p, num_parts, precision, ue, stream);
+  return launch_ring_any<512, 4, 3>(p, num_parts, precision, ue, stream);
 }
 
 }  // namespace sda

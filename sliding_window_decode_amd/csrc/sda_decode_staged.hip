@@ -113,7 +113,7 @@ void decode_kernel(DecodeParams p) {
 
   // ---- record staging (registers): the sub-tile's data chunks, its scale chunk and rope chunk
   u32x4 stg[4];
-  uint32_t stg_sb[2];
+  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; FP8_UE8M0: the word holding its ue8m0 byte
   u32x4 stg_sc;
   u32x4 stg_rp;
   auto rec_issue = [&](const Item& it, int s) {
@@ -134,8 +134,10 @@ void decode_kernel(DecodeParams p) {
         const int r = (tid >> 5) + 8 * k, c = tid & 31;
         const uint64_t a = sm.addr[s][r];
         stg[k] = ld_global_16(a ? a + 16 * c : dummy);
+        // chunk c (dims 16c .. 16c+15) takes scale byte c / 2: byte (c / 2) % 4 of word c / 8
+        if (ld.format == SDA_FP8_UE8M0) stg_sb[k] = *(gbl_u32*)(a ? a + 512 + 4 * (c >> 3) : dummy);
       }
-      if (tid < KT) {
+      if (tid < KT && ld.format != SDA_FP8_UE8M0) {
         const uint64_t sa = sm.saddr[s][tid];
         if (ld.format == SDA_FP8_SLOTSCALE)
           stg_sc[0] = *(gbl_u32*)(sa ? sa : dummy);
@@ -179,16 +181,20 @@ void decode_kernel(DecodeParams p) {
         *(f32x4*)sm.scale[tid] = f32x4{v, v, v, v};
       }
     } else {
+      const bool ue8m0 = ld.format == SDA_FP8_UE8M0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int r = (tid >> 5) + 8 * k, c = tid & 31;
         const bool ok = sm.addr[s][r] != 0;
         const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
+        // ue8m0 records: the power-of-two scale is applied by the conversion (the row's scale table
+        // then holds 1); other formats convert unscaled
+        const float cs = ue8m0 ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 1) & 3))) : 1.0f;
         uint32_t y[8];
-        e4m3x4_to_bf16(x[0], y[0], y[1]);
-        e4m3x4_to_bf16(x[1], y[2], y[3]);
-        e4m3x4_to_bf16(x[2], y[4], y[5]);
-        e4m3x4_to_bf16(x[3], y[6], y[7]);
+        e4m3x4_to_bf16_scaled(x[0], cs, y[0], y[1]);
+        e4m3x4_to_bf16_scaled(x[1], cs, y[2], y[3]);
+        e4m3x4_to_bf16_scaled(x[2], cs, y[4], y[5]);
+        e4m3x4_to_bf16_scaled(x[3], cs, y[6], y[7]);
         const int f = ((r & 3) << 1) | ((r >> 2) & 1);
         char* row = sm.tile + r * RS;
         const int c0 = 2 * c, c1 = 2 * c + 1;
@@ -201,6 +207,8 @@ void decode_kernel(DecodeParams p) {
         if (ld.format == SDA_FP8_SLOTSCALE) {
           const float v = __builtin_bit_cast(float, stg_sc[0]);
           sc = f32x4{v, v, v, v};
+        } else if (ue8m0) {
+          sc = f32x4{1.f, 1.f, 1.f, 1.f};
         } else {
           sc = __builtin_bit_cast(f32x4, stg_sc);
         }

@@ -38,6 +38,17 @@ __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_
   hi = __builtin_bit_cast(uint32_t, b);
 }
 
+// The same with a power-of-two scale applied by the conversion: the scale operand contributes only
+// its exponent, so passing the float with exponent field e (and no mantissa) multiplies by 2^(e - 127)
+// -- an ue8m0 scale byte e used as it is. Exact while the products stay within the bf16 range.
+__device__ __forceinline__ float ue8m0_scale(uint32_t byte) { return __builtin_bit_cast(float, (byte & 0xFFu) << 23); }
+__device__ __forceinline__ void e4m3x4_to_bf16_scaled(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) { return __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0]; }
 
 // Two e2m1 codes of byte `SEL` of w (low nibble first) times an e4m3 block scale, as a packed bf16
@@ -152,6 +163,17 @@ __device__ __forceinline__ int lds_ld_i32(uint32_t lds_addr) {
   int r;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr) : "memory");
   return r;
+}
+
+// 16 e4m3 codes times 2^(e - 127) -> two bf16x8 (the scaled conversion above).
+__device__ __forceinline__ void e4m3x16_to_bf16_scaled(const u32x4 x, float scale, bf16x8& lo, bf16x8& hi) {
+  uint32_t y[8];
+  e4m3x4_to_bf16_scaled(x[0], scale, y[0], y[1]);
+  e4m3x4_to_bf16_scaled(x[1], scale, y[2], y[3]);
+  e4m3x4_to_bf16_scaled(x[2], scale, y[4], y[5]);
+  e4m3x4_to_bf16_scaled(x[3], scale, y[6], y[7]);
+  lo = __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
+  hi = __builtin_bit_cast(bf16x8, u32x4{y[4], y[5], y[6], y[7]});
 }
 
 // 16 e4m3 codes -> two bf16x8 (codes 0..7, 8..15), exact.

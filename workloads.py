@@ -230,7 +230,7 @@ def make_sink(rng: np.random.Generator, H: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- the five configurations
 
-CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32")
+CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32", "c6_swa_ue8m0")
 
 
 def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Workload:
@@ -245,6 +245,8 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
                      extra width 2048 over a 262144-slot NVFP4_288 cache; lens U{1..W}; sink.
     c5_topk_v32      128 tokens, 128 heads, d_qk 576; top-k width 2048 over a 131072-slot
                      V32_656 cache; lens = 2048; sink; scale 1/sqrt(576).
+    c6_swa_ue8m0     c3's shape with both caches in FP8_UE8M0 (the fp8 record with one power-of-two
+                     scale per 32 dims); a measurement workload for that format, not one of the five.
     All pages hold 64 slots.
     """
     rng = np.random.default_rng(seed)
@@ -291,6 +293,16 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
         lst = make_list(rng, T, W, 131072, W, W)
         sink = make_sink(rng, H)
         return Workload(name, T, H, 576, 512, q, cache, lst, None, None, sink, float(np.float32(1 / math.sqrt(576))))
+    if name == "c6_swa_ue8m0":
+        T = 256 if T is None else T
+        H = 32
+        q = make_q(rng, T, H, 512)
+        cache = make_cache(rng, FP8_UE8M0, 32768, 64, pad)
+        xcache = make_cache(rng, FP8_UE8M0, 65536, 64, pad)
+        lst = make_list(rng, T, 128, 32768, 1, 128)
+        xlst = make_list(rng, T, 512, 65536, 1, 512)
+        sink = make_sink(rng, H)
+        return Workload(name, T, H, 512, 512, q, cache, lst, xcache, xlst, sink, float(np.float32(1 / math.sqrt(512))))
     raise ValueError(f"unknown workload {name!r}")
 
 
