@@ -45,7 +45,8 @@ def algorithmic_work(w):
     rows = 0
     byts = w.T * w.H * w.d_qk * 2 + w.T * w.H * w.d_v * 2 + w.T * w.H * 4
     for cache, L in w.lists():
-        n = np.clip(L.lens, 0, L.width) if L.lens is not None else np.full(w.T, L.width)
+        qpl = max(1, getattr(L, "queries_per_len", 1))
+        n = np.clip(L.lens[np.arange(w.T) // qpl], 0, L.width) if L.lens is not None else np.full(w.T, L.width)
         for t in range(w.T):
             sids = L.idx[t, :n[t]]
             valid = int(((sids >= 0) & (sids < cache.num_slots)).sum())

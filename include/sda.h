@@ -85,13 +85,17 @@ typedef struct sda_cache {
 } sda_cache;
 
 /* A per-token slot list: idx[t * row_stride + j] for j < width is the slot id at list position j of
- * token t (-1 = none); lens[t] (or width when lens is NULL) is the number of leading positions that
- * take part. row_stride >= width; metadata buffers may hold more rows than tokens. */
+ * token t (-1 = none); lens[t / queries_per_len] (or width when lens is NULL) is the number of leading
+ * positions that take part. row_stride >= width; metadata buffers may hold more rows than tokens.
+ * queries_per_len: consecutive tokens that share one length entry -- the s_q queries of a request
+ * when q is [b][s_q][H][d] and the lengths are per request [b] (FlashMLA sparse_decode.h,
+ * sparse_attn_decode_interface: topk_length [b] with indices [b][s_q][topk]); 0 or 1: one entry per
+ * token. Negative values are an error. */
 typedef struct sda_list {
   const int32_t* idx;
   int64_t row_stride;
   int32_t width;
-  int32_t reserved;
+  int32_t queries_per_len;
   const int32_t* lens;
 } sda_list;
 
@@ -145,9 +149,10 @@ int sda_get_sched_meta(int T, const sda_list* list /*host*/, const sda_list* ext
                        const sda_plan* plan /*host*/, int32_t* meta, int32_t* num_splits, void* stream);
 
 /* Host only. The same schedule as sda_get_sched_meta, computed on the calling thread from host
- * copies of the lengths (lens / extra_lens: [T] int32 or NULL = width) into host arrays meta
- * [num_parts][SDA_META_INTS] and num_splits [T+1]. For callers that keep lengths on the host. */
-int sda_get_sched_meta_host(int T, const int32_t* lens /*host, nullable*/, int width,
+ * copies of the lengths (lens / extra_lens: one int32 per queries_per_len tokens, as in sda_list, or
+ * NULL = width) into host arrays meta [num_parts][SDA_META_INTS] and num_splits [T+1]. For callers
+ * that keep lengths on the host. */
+int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens /*host, nullable*/, int width,
                             const int32_t* extra_lens /*host, nullable*/, int extra_width /*0 = no extra list*/,
                             const sda_plan* plan /*host*/, int32_t* meta /*host*/, int32_t* num_splits /*host*/);
 

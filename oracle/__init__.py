@@ -76,9 +76,22 @@ def _cache_struct(c, keep):
     return OrcCache(data.ctypes.data, c.num_pages, c.page_size, c.page_stride, c.fmt, _ptr(ss))
 
 
-def _list_struct(L, keep, t0=0, t1=None):
+def token_lens(L, T: int) -> Optional[np.ndarray]:
+    """Per-token lengths of list L over T tokens: token t takes entry t // queries_per_len (the queries
+    of one request share its length: FlashMLA sparse_decode.h, topk_length [b] for indices [b][s_q])."""
+    if L.lens is None:
+        return None
+    qpl = max(1, int(getattr(L, "queries_per_len", 1)))
+    lens = np.asarray(L.lens, dtype=np.int32)
+    if len(lens) < -(-T // qpl):
+        raise ValueError("lengths hold fewer entries than the tokens need")
+    return lens[np.arange(T) // qpl]
+
+
+def _list_struct(L, keep, T, t0=0, t1=None):
     idx = np.ascontiguousarray(L.idx[t0:t1], dtype=np.int32)
-    lens = None if L.lens is None else np.ascontiguousarray(L.lens[t0:t1], dtype=np.int32)
+    lt = token_lens(L, T)
+    lens = None if lt is None else np.ascontiguousarray(lt[t0:t1], dtype=np.int32)
     keep += [idx, lens]
     return OrcList(idx.ctypes.data, idx.shape[1], L.width, _ptr(lens))
 
@@ -100,11 +113,11 @@ def attention(w, tokens: Optional[slice] = None, nthreads: int = 1, sink="defaul
     q = np.ascontiguousarray(w.q[t0:t1], dtype=np.uint16)
     keep.append(q)
     cs = _cache_struct(w.cache, keep)
-    ls = _list_struct(w.lst, keep, t0, t1)
+    ls = _list_struct(w.lst, keep, w.T, t0, t1)
     xcs = xls = None
     if w.xcache is not None:
         xcs = _cache_struct(w.xcache, keep)
-        xls = _list_struct(w.xlst, keep, t0, t1)
+        xls = _list_struct(w.xlst, keep, w.T, t0, t1)
     snk = w.sink if isinstance(sink, str) else sink
     snk = None if snk is None else np.ascontiguousarray(snk, dtype=np.float32)
     keep.append(snk)

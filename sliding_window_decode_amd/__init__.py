@@ -39,7 +39,7 @@ class sda_cache(ctypes.Structure):
 
 class sda_list(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("row_stride", ctypes.c_int64), ("width", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("lens", ctypes.c_void_p)]
+                ("queries_per_len", ctypes.c_int32), ("lens", ctypes.c_void_p)]
 
 
 class sda_plan(ctypes.Structure):
@@ -68,7 +68,7 @@ def lib():
         L.sda_workspace_bytes.restype = sz
         L.sda_get_sched_meta.argtypes = [i32, ctypes.POINTER(sda_list), ctypes.POINTER(sda_list),
                                          ctypes.POINTER(sda_plan), vp, vp, vp]
-        L.sda_get_sched_meta_host.argtypes = [i32, vp, i32, vp, i32, ctypes.POINTER(sda_plan), vp, vp]
+        L.sda_get_sched_meta_host.argtypes = [i32, i32, vp, i32, vp, i32, ctypes.POINTER(sda_plan), vp, vp]
         L.sda_sparse_decode_attn.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.POINTER(sda_cache),
                                              ctypes.POINTER(sda_list), ctypes.POINTER(sda_cache),
                                              ctypes.POINTER(sda_list), vp, ctypes.c_float, ctypes.POINTER(sda_plan),
@@ -122,10 +122,11 @@ class Cache:
 class SlotList:
     idx: "object"                 # torch int32 [T, row_stride] (device)
     width: int
-    lens: "object" = None         # torch int32 [T] (device) or None
+    lens: "object" = None         # torch int32 [ceil(T / queries_per_len)] (device) or None
+    queries_per_len: int = 1      # consecutive tokens (queries of one request) sharing a length entry
 
     def c(self) -> sda_list:
-        return sda_list(_ptr(self.idx), self.idx.stride(0), self.width, 0, _ptr(self.lens))
+        return sda_list(_ptr(self.idx), self.idx.stride(0), self.width, self.queries_per_len, _ptr(self.lens))
 
 
 def make_plan(T: int, H: int, d_qk: int, width: int, extra_width: int = 0, num_cus: int = 256) -> sda_plan:
@@ -145,14 +146,16 @@ def get_sched_meta(T: int, lst: SlotList, extra: Optional[SlotList], plan: sda_p
                                     ctypes.byref(plan), _ptr(meta), _ptr(num_splits), _stream(stream)))
 
 
-def get_sched_meta_host(T: int, lens, width: int, extra_lens, extra_width: int, plan: sda_plan):
-    """Host schedule from numpy int32 lengths (or None): returns (meta [P, 8], num_splits [T+1]) numpy arrays."""
+def get_sched_meta_host(T: int, lens, width: int, extra_lens, extra_width: int, plan: sda_plan,
+                        queries_per_len: int = 1):
+    """Host schedule from numpy int32 lengths (or None; one entry per queries_per_len tokens): returns
+    (meta [P, 8], num_splits [T+1]) numpy arrays."""
     import numpy as np
     meta = np.zeros((plan.num_parts, META_INTS), dtype=np.int32)
     ns = np.zeros(T + 1, dtype=np.int32)
     l0 = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
     l1 = None if extra_lens is None else np.ascontiguousarray(extra_lens, dtype=np.int32)
-    _check(lib().sda_get_sched_meta_host(T, None if l0 is None else l0.ctypes.data, width,
+    _check(lib().sda_get_sched_meta_host(T, queries_per_len, None if l0 is None else l0.ctypes.data, width,
                                          None if l1 is None else l1.ctypes.data, extra_width, ctypes.byref(plan),
                                          meta.ctypes.data, ns.ctypes.data))
     return meta, ns

@@ -78,8 +78,15 @@ int check_list(const sda_list* l, const char* which) {
     snprintf(msg, sizeof(msg), "%s list: width must be >= 1 and row_stride >= width", which);
     return fail(SDA_ERR_INVALID_ARG, msg);
   }
+  if (l->queries_per_len < 0) {
+    snprintf(msg, sizeof(msg), "%s list: queries_per_len must be >= 0", which);
+    return fail(SDA_ERR_INVALID_ARG, msg);
+  }
   return SDA_OK;
 }
+
+// Tokens per length entry of a list (0 means one entry per token).
+int lens_div(const sda_list* l) { return l->queries_per_len > 1 ? l->queries_per_len : 1; }
 
 int check_plan(const sda_plan* plan, int H) {
   if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
@@ -122,6 +129,7 @@ sda::ListDev list_dev(const sda_cache* c, const sda_list* l) {
   d.page_shift = ilog2(c->page_size);
   d.format = c->format;
   d.rec = sda_record_bytes(c->format);
+  d.lens_div = lens_div(l);
   return d;
 }
 
@@ -148,10 +156,12 @@ sda::SchedParams sched_params(int T, const sda_list* list, const sda_list* extra
   sda::SchedParams s;
   memset(&s, 0, sizeof(s));
   s.lens[0] = list->lens;
+  s.lens_div[0] = lens_div(list);
   s.width[0] = list->width;
   s.nlists = 1;
   if (extra) {
     s.lens[1] = extra->lens;
+    s.lens_div[1] = lens_div(extra);
     s.width[1] = extra->width;
     s.nlists = 2;
   }
@@ -246,24 +256,26 @@ int sda_get_sched_meta(int T, const sda_list* list, const sda_list* extra, const
   return SDA_OK;
 }
 
-int sda_get_sched_meta_host(int T, const int32_t* lens, int width, const int32_t* extra_lens, int extra_width,
-                            const sda_plan* plan, int32_t* meta, int32_t* num_splits) {
+int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens, int width, const int32_t* extra_lens,
+                            int extra_width, const sda_plan* plan, int32_t* meta, int32_t* num_splits) {
   if (T < 1 || width < 1 || extra_width < 0) return fail(SDA_ERR_INVALID_ARG, "T and width must be >= 1");
+  if (queries_per_len < 0) return fail(SDA_ERR_INVALID_ARG, "queries_per_len must be >= 0");
+  const int div = queries_per_len > 1 ? queries_per_len : 1;
   if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
   if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
   const int P = plan->num_parts, F = plan->fixed_overhead;
   int64_t total = 0;
   for (int t = 0; t < T; ++t) {
-    const int n0 = sda::clamp_len(lens, width, t);
-    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, extra_width, t) : 0;
+    const int n0 = sda::clamp_len(lens, div, width, t);
+    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, div, extra_width, t) : 0;
     total += sda::token_tiles(n0, n1) + F;
   }
   const int64_t Q = sda::part_quantum(total, P);
   int64_t cum = 0;
   int32_t splits = 0;
   for (int t = 0; t < T; ++t) {
-    const int n0 = sda::clamp_len(lens, width, t);
-    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, extra_width, t) : 0;
+    const int n0 = sda::clamp_len(lens, div, width, t);
+    const int n1 = extra_width > 0 ? sda::clamp_len(extra_lens, div, extra_width, t) : 0;
     const int nt = sda::token_tiles(n0, n1);
     const int64_t pos0 = cum + F;
     const int64_t p0 = pos0 / Q, p1 = (pos0 + nt - 1) / Q;

@@ -137,34 +137,6 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Global stores issued as inline assembly. The compiler then sees only loads among this wave's
-// pending vector-memory operations, and counts them exactly where it must wait for one (pending loads
-// and stores together make it wait for all of them). A wait on a load must then count loads only:
-// stores may complete in any order relative to loads.
-__device__ __forceinline__ void st_global_u16(void* p, uint32_t v) {
-  asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void st_global_f32(void* p, float v) {
-  asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
-}
-
-// 16-byte global load the compiler does not track: r receives the data when the load completes.
-// The caller must wait for it by count (vmcnt) and then name r as an operand of an inline-assembly
-// statement, so that no use of r is placed above the wait. r is tied to its previous register, so
-// the load lands where r already lives.
-__device__ __forceinline__ void ld_global_b128_untracked(bf16x8& r, const void* p) {
-  asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(r) : "v"(p) : "memory");
-}
-
-// ds_read_b32 and its wait in one statement, so the value is complete when the statement ends. For
-// words written by a global -> LDS load, after an explicit vmcnt wait: the compiler does not see
-// that dependence, and a builtin read would make it drain every such load in flight instead.
-__device__ __forceinline__ int lds_ld_i32(uint32_t lds_addr) {
-  int r;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr) : "memory");
-  return r;
-}
-
 // 16 e4m3 codes times 2^(e - 127) -> two bf16x8 (the scaled conversion above).
 __device__ __forceinline__ void e4m3x16_to_bf16_scaled(const u32x4 x, float scale, bf16x8& lo, bf16x8& hi) {
   uint32_t y[8];
@@ -172,17 +144,6 @@ __device__ __forceinline__ void e4m3x16_to_bf16_scaled(const u32x4 x, float scal
   e4m3x4_to_bf16_scaled(x[1], scale, y[2], y[3]);
   e4m3x4_to_bf16_scaled(x[2], scale, y[4], y[5]);
   e4m3x4_to_bf16_scaled(x[3], scale, y[6], y[7]);
-  lo = __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
-  hi = __builtin_bit_cast(bf16x8, u32x4{y[4], y[5], y[6], y[7]});
-}
-
-// 16 e4m3 codes -> two bf16x8 (codes 0..7, 8..15), exact.
-__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 x, bf16x8& lo, bf16x8& hi) {
-  uint32_t y[8];
-  e4m3x4_to_bf16(x[0], y[0], y[1]);
-  e4m3x4_to_bf16(x[1], y[2], y[3]);
-  e4m3x4_to_bf16(x[2], y[4], y[5]);
-  e4m3x4_to_bf16(x[3], y[6], y[7]);
   lo = __builtin_bit_cast(bf16x8, u32x4{y[0], y[1], y[2], y[3]});
   hi = __builtin_bit_cast(bf16x8, u32x4{y[4], y[5], y[6], y[7]});
 }

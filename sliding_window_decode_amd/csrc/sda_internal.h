@@ -25,7 +25,7 @@ struct ListDev {
   int32_t page_shift;
   int32_t format;
   int32_t rec;               // record bytes
-  int32_t pad_;
+  int32_t lens_div;          // tokens per length entry (>= 1)
 };
 
 struct DecodeParams {
@@ -48,6 +48,7 @@ struct DecodeParams {
 
 struct SchedParams {
   const int32_t* lens[2];    // nullptr = width
+  int32_t lens_div[2];       // tokens per length entry (>= 1)
   int32_t width[2];
   int nlists;
   int T;
@@ -76,8 +77,9 @@ struct CombineParams {
 // cum(t) + F + i and belongs to part floor(position / Q) with Q = ceil(total / num_parts). Parts are
 // therefore contiguous ranges of the (token, tile) sequence, in order.
 
-__host__ __device__ inline int clamp_len(const int32_t* lens, int width, int t) {
-  int n = lens ? lens[t] : width;
+// Clamped length of token t (lens holds one entry per `div` consecutive tokens).
+__host__ __device__ inline int clamp_len(const int32_t* lens, int div, int width, int t) {
+  int n = lens ? lens[t / div] : width;
   return n < 0 ? 0 : (n > width ? width : n);
 }
 

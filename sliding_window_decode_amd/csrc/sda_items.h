@@ -8,8 +8,7 @@
 //
 // The part's first token comes with its lengths and split index in the meta record, so that walking
 // starts without a memory round trip. The lengths and split index of each later token are fetched
-// when the walker enters the token before it, through a source the kernel chooses (registers, or
-// LDS filled by a global -> LDS load), so that they have long arrived when they are used.
+// when the walker enters the token before it, so that they have long arrived when they are used.
 #pragma once
 
 #include "sda_device.h"
@@ -44,37 +43,11 @@ struct TokenInfoRegs {
   TokenInfo x;
   __device__ __forceinline__ void issue(const DecodeParams& p, int t) {
     const int tz = t + opaque_lane_zero();
-    x.r0 = p.lst[0].lens ? p.lst[0].lens[tz] : p.lst[0].width;
-    x.r1 = p.nlists > 1 ? (p.lst[1].lens ? p.lst[1].lens[tz] : p.lst[1].width) : 0;
+    x.r0 = p.lst[0].lens ? p.lst[0].lens[tz / p.lst[0].lens_div] : p.lst[0].width;
+    x.r1 = p.nlists > 1 ? (p.lst[1].lens ? p.lst[1].lens[tz / p.lst[1].lens_div] : p.lst[1].width) : 0;
     x.s0 = p.num_splits[tz];
   }
   __device__ __forceinline__ TokenInfo fetch(const DecodeParams&) const { return x; }
-};
-
-// Token information through LDS: lanes 0..2 of the wave load the three words into `buf` (this
-// wave's 16 bytes, two alternating slots). The caller must wait for the load (one global operation;
-// `fresh` is set when one is issued) before the walker fetches it.
-struct TokenInfoLds {
-  int32_t* buf;  // [2][4] words of this wave
-  int slot;
-  int fresh;
-  __device__ __forceinline__ void issue(const DecodeParams& p, int t) {
-    const int lane = threadIdx.x & 63;
-    slot ^= 1;
-    const int32_t* src = p.num_splits + t;  // lane 2; also read (and not used) by lanes 0, 1 without lengths
-    if (lane == 0 && p.lst[0].lens) src = p.lst[0].lens + t;
-    if (lane == 1 && p.nlists > 1 && p.lst[1].lens) src = p.lst[1].lens + t;
-    if (lane < 3) dma4((uint64_t)src, buf + 4 * slot);
-    fresh = 1;
-  }
-  __device__ __forceinline__ TokenInfo fetch(const DecodeParams& p) const {
-    const uint32_t a = lds_u32(buf + 4 * slot);
-    TokenInfo x;
-    x.r0 = p.lst[0].lens ? lds_ld_i32(a) : p.lst[0].width;
-    x.r1 = p.nlists > 1 ? (p.lst[1].lens ? lds_ld_i32(a + 4) : p.lst[1].width) : 0;
-    x.s0 = lds_ld_i32(a + 8);
-    return x;
-  }
 };
 
 struct ItemGen {

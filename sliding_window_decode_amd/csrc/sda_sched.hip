@@ -42,8 +42,8 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
   const int NT = blockDim.x;
   int local = 0;
   for (int t = tid; t < p.T; t += NT) {
-    const int n0 = clamp_len(p.lens[0], p.width[0], t);
-    const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
+    const int n0 = clamp_len(p.lens[0], p.lens_div[0], p.width[0], t);
+    const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], t) : 0;
     local += token_tiles(n0, n1) + p.F;
   }
   int total = 0;
@@ -54,8 +54,8 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
     const int t = base + tid;
     int nt = 0, cost = 0, n0 = 0, n1 = 0;
     if (t < p.T) {
-      n0 = clamp_len(p.lens[0], p.width[0], t);
-      n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.width[1], t) : 0;
+      n0 = clamp_len(p.lens[0], p.lens_div[0], p.width[0], t);
+      n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], t) : 0;
       nt = token_tiles(n0, n1);
       cost = nt + p.F;
     }

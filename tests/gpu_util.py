@@ -21,7 +21,8 @@ def dev_cache(c, device="cuda"):
 
 def dev_list(L, device="cuda"):
     return sda.SlotList(torch.from_numpy(np.ascontiguousarray(L.idx)).to(device), L.width,
-                        None if L.lens is None else torch.from_numpy(L.lens).to(device))
+                        None if L.lens is None else torch.from_numpy(L.lens).to(device),
+                        getattr(L, "queries_per_len", 1))
 
 
 def dev_q(w, device="cuda"):

@@ -85,7 +85,8 @@ def valid_rows(w, t: int):
     """(cache, sid) pairs of token t's valid rows, main list first, in list order."""
     rows = []
     for cache, L in w.lists():
-        n = L.width if L.lens is None else int(np.clip(L.lens[t], 0, L.width))
+        qpl = max(1, getattr(L, "queries_per_len", 1))
+        n = L.width if L.lens is None else int(np.clip(L.lens[t // qpl], 0, L.width))
         for j in range(n):
             sid = int(L.idx[t, j])
             if 0 <= sid < cache.num_slots:

@@ -82,13 +82,13 @@ class _FakeTensor:
 
 
 def _call(q_shape=(4, 16, 512), fmt=sda.FP8_528, page_size=64, page_stride=None, width=128, H_out=16,
-          extra=False, xfmt=None, plan=None, ws_bytes=None, q_ptr=1 << 20, slot_scale=False, meta=None):
+          extra=False, xfmt=None, plan=None, ws_bytes=None, q_ptr=1 << 20, slot_scale=False, meta=None, qpl=1):
     T, H, dqk = q_shape
     q = _FakeTensor(q_shape, ptr=q_ptr)
     rec = {0: 512, 1: 528, 2: 288, 3: 656}.get(fmt, 512)
     cache = sda.Cache(_FakeTensor((1,), 1 << 24), 16, page_size, page_stride or page_size * rec, fmt,
                       _FakeTensor((1,), 1 << 26) if slot_scale else None)
-    lst = sda.SlotList(_FakeTensor((T, width), 1 << 27), width, None)
+    lst = sda.SlotList(_FakeTensor((T, width), 1 << 27), width, None, qpl)
     xc = xl = None
     if extra:
         xrec = {0: 512, 1: 528, 2: 288, 3: 656}[xfmt]
@@ -115,6 +115,7 @@ def _call(q_shape=(4, 16, 512), fmt=sda.FP8_528, page_size=64, page_stride=None,
     (dict(slot_scale=True), sda.SDA_ERR_INVALID_ARG),                      # slot scale given for fp8_528
     (dict(fmt=7), sda.SDA_ERR_UNSUPPORTED),                                # unknown format
     (dict(width=0), sda.SDA_ERR_INVALID_ARG),                              # width
+    (dict(qpl=-2), sda.SDA_ERR_INVALID_ARG),                               # queries_per_len
     (dict(extra=True, xfmt=sda.V32_656), sda.SDA_ERR_UNSUPPORTED),         # extra cache d_qk mismatch
     (dict(plan=sda.sda_plan(0, 16, 2, 3)), sda.SDA_ERR_INVALID_ARG),       # num_parts
     (dict(plan=sda.sda_plan(8, 24, 2, 3)), sda.SDA_ERR_UNSUPPORTED),       # heads per group
@@ -237,3 +238,29 @@ def test_host_scheduler_balances_cost():
         b = seq_pos[bt] + bi if bt < T else seq_pos[T]
         e = seq_pos[et] + ei if et < T else seq_pos[T]
         assert e - b <= Q
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("qpl", [0, 1, 2, 3, 7])
+def test_host_scheduler_grouped_lengths_equal_expanded(seed, qpl):
+    """A length entry shared by queries_per_len consecutive tokens schedules exactly like the same
+    length repeated per token (the s_q queries of a request share its length)."""
+    rng = np.random.default_rng(100 + seed)
+    T = int(rng.integers(1, 200))
+    g = max(qpl, 1)
+    W, X = 128, 512
+    nreq = -(-T // g)
+    lens = rng.integers(-3, W + 5, size=nreq).astype(np.int32)
+    xl = rng.integers(0, X + 3, size=nreq).astype(np.int32)
+    plan = sda.sda_plan(int(rng.choice([3, 64, 256])), 16, 2, 3)
+    m_g, ns_g = sda.get_sched_meta_host(T, lens, W, xl, X, plan, queries_per_len=qpl)
+    e = np.arange(T) // g
+    m_e, ns_e = sda.get_sched_meta_host(T, lens[e], W, xl[e], X, plan)
+    assert np.array_equal(m_g, m_e) and np.array_equal(ns_g, ns_e)
+
+
+def test_host_scheduler_rejects_negative_queries_per_len():
+    plan = sda.sda_plan(4, 16, 2, 3)
+    with pytest.raises(sda.SdaError) as ei:
+        sda.get_sched_meta_host(4, None, 128, None, 0, plan, queries_per_len=-1)
+    assert ei.value.status == sda.SDA_ERR_INVALID_ARG

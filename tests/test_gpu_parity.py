@@ -363,3 +363,33 @@ def test_repeat_runs_are_bitwise_identical():
     o1, l1, _ = dw.run()
     o2, l2, _ = dw.run()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ requests of several queries
+
+@pytest.mark.parametrize("fmt,xfmt,H,qpl", [(wl.FP8_528, wl.FP8_528, 64, 2), (wl.FP8_528, None, 128, 4),
+                                            (wl.FP8_UE8M0, wl.FP8_UE8M0, 32, 3), (wl.FP8_528, wl.NVFP4_288, 16, 5),
+                                            (wl.V32_656, None, 64, 2)])
+def test_request_lengths_shared_by_queries(fmt, xfmt, H, qpl):
+    """Lengths per request shared by its s_q queries (queries_per_len) give bit-identical results to the
+    same lengths repeated per token, and match the oracle; the token count leaves a ragged last request."""
+    T = 4 * qpl + 1
+    _log(f"[requests] fmt={fmt} xfmt={xfmt} H={H} s_q={qpl} T={T}")
+    kw = dict(T=T, H=H, width=128, num_slots=4096, sink=True, p_invalid=0.05, lens_lo=0)
+    if xfmt is not None:
+        kw["xwidth"] = 320
+    w = wl.small_workload(80 + qpl, fmt, xfmt, **kw)
+    rng = np.random.default_rng(qpl)
+    nreq = -(-T // qpl)
+    g = copy.deepcopy(w)
+    for L in [g.lst] + ([g.xlst] if xfmt is not None else []):
+        L.lens = rng.integers(0, L.width + 1, size=nreq).astype(np.int32)
+        L.queries_per_len = qpl
+    e = copy.deepcopy(w)
+    r = np.arange(T) // qpl
+    e.lst.lens = g.lst.lens[r].copy()
+    if xfmt is not None:
+        e.xlst.lens = g.xlst.lens[r].copy()
+    _, out_g, lse_g = _run_cmp(g, f"grouped s_q={qpl}")
+    out_e, lse_e, _ = DeviceWorkload(e).run()
+    assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)

@@ -271,6 +271,33 @@ def test_entries_beyond_lens_are_ignored_and_lens_clamp(orc):
     assert np.all(o5 == 0) and np.all(l5 == -np.inf)
 
 
+@pytest.mark.parametrize("qpl", [2, 3])
+def test_request_lengths_shared_by_its_queries(orc, qpl):
+    """Lengths per request [b] with q [b][s_q] (FlashMLA sparse_decode.h, topk_length): query t of the
+    flattened tokens uses entry t // s_q; positions past it are ignored for every query of the request."""
+    w = _w(31, xfmt=wl.FP8_528, sink=True, T=7)
+    nreq = -(-w.T // qpl)
+    rng = np.random.default_rng(31)
+    g = copy.deepcopy(w)
+    g.lst.lens = rng.integers(0, w.lst.width + 1, size=nreq).astype(np.int32)
+    g.xlst.lens = rng.integers(0, w.xlst.width + 1, size=nreq).astype(np.int32)
+    g.lst.queries_per_len = g.xlst.queries_per_len = qpl
+    e = copy.deepcopy(w)
+    r = np.arange(w.T) // qpl
+    e.lst.lens, e.xlst.lens = g.lst.lens[r].copy(), g.xlst.lens[r].copy()
+    og, lg = orc.attention(g)
+    oe, le = orc.attention(e)
+    np.testing.assert_array_equal(og, oe)
+    np.testing.assert_array_equal(lg, le)
+    for t in range(w.T):
+        n = int(g.lst.lens[t // qpl])
+        g.lst.idx[t, n:] = rng.integers(0, w.cache.num_slots, size=w.lst.width - n)
+    np.testing.assert_array_equal(orc.attention(g)[0], og)
+    g.lst.lens = g.lst.lens[:nreq - 1]
+    with pytest.raises(ValueError):
+        orc.attention(g)
+
+
 def test_lens_zero_gives_zero_output_and_sink_lse(orc):
     w = _w(5, sink=True)
     w.lst.lens[:] = 0

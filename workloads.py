@@ -69,7 +69,8 @@ class Cache:
 class SlotList:
     idx: np.ndarray             # int32 [T, row_stride]; only the first `width` columns are read
     width: int
-    lens: Optional[np.ndarray]  # int32 [T] or None (= width)
+    lens: Optional[np.ndarray]  # int32 [ceil(T / queries_per_len)] or None (= width)
+    queries_per_len: int = 1    # consecutive tokens (the queries of one request) sharing a length entry
 
 
 @dataclasses.dataclass
