@@ -65,9 +65,16 @@ enum sda_status {
  * SDA_FP8_UE8M0      528 B: 512 e4m3fn codes, then 16 ue8m0 scale bytes, byte g the power of two
  *                    2^(g - 127) covering dims [32g, 32g+32) (vLLM swapab_decode_attn, stage_inputs,
  *                    fp8 branch); byte 255 (NaN in the MX encoding) gives NaN rows.
- * A decoded value is code * scale (exact in bf16 for every format; for SDA_FP8_UE8M0 while it stays
- * within the bf16 range). */
-enum sda_format { SDA_FP8_SLOTSCALE = 0, SDA_FP8_528 = 1, SDA_NVFP4_288 = 2, SDA_V32_656 = 3, SDA_FP8_UE8M0 = 4 };
+ * SDA_MODEL1_584     584 B, d_qk = d_v = 512: 448 e4m3fn codes (dims 0..447), 64 little-endian bf16
+ *                    values (dims 448..511), 7 ue8m0 scale bytes (byte g covering dims [64g, 64g+64)),
+ *                    one unused byte (FlashMLA sparse_decode.h: MODEL1 bytes_per_token; the page gives
+ *                    the parts and their sum, and they are laid out in the order of that sum). The
+ *                    value rows are the whole 512 dims, the bf16 ones included. Records start 8-byte
+ *                    aligned.
+ * A decoded value is code * scale (exact in bf16 for every format; for the ue8m0 formats while it
+ * stays within the bf16 range). */
+enum sda_format { SDA_FP8_SLOTSCALE = 0, SDA_FP8_528 = 1, SDA_NVFP4_288 = 2, SDA_V32_656 = 3, SDA_FP8_UE8M0 = 4,
+                  SDA_MODEL1_584 = 5 };
 
 /* A paged cache. Slot id s lives in page s / page_size at offset s % page_size; its record starts
  * at base + (s / page_size) * page_stride + (s % page_size) * record_bytes. Pages may be further

@@ -67,6 +67,7 @@ int orc_record_bytes(int format) {
     case ORC_NVFP4_288: return 256 + 32;        /* packed e2m1, then one e4m3 per 16 dims  */
     case ORC_V32_656: return 512 + 4 * 4 + 64 * 2; /* codes, 4 fp32 scales, 64 bf16 dims   */
     case ORC_FP8_UE8M0: return 512 + 16;        /* codes, then one ue8m0 per 32 dims       */
+    case ORC_MODEL1_584: return 448 + 64 * 2 + 448 / 64 + 1; /* codes, 64 bf16 dims, 7 ue8m0, pad */
     default: return -1;
   }
 }
@@ -76,7 +77,8 @@ int orc_record_dims(int format) {
     case ORC_FP8_SLOTSCALE:
     case ORC_FP8_528:
     case ORC_NVFP4_288:
-    case ORC_FP8_UE8M0: return 512;
+    case ORC_FP8_UE8M0:
+    case ORC_MODEL1_584: return 512;
     case ORC_V32_656: return 576;
     default: return -1;
   }
@@ -111,6 +113,16 @@ int orc_decode_slot(const orc_cache* c, int64_t sid, double* k) {
        * holds dims 16c..16c+15 and takes scale byte c / 2, i.e. scale byte g
        * covers dims 32g..32g+31 */
       for (d = 0; d < 512; d++) k[d] = orc_e4m3(r[d]) * orc_ue8m0(r[512 + d / 32]);
+      break;
+    }
+    case ORC_MODEL1_584: {
+      /* FlashMLA sparse_decode.h, MODEL1 bytes_per_token: 448 e4m3 codes, 64 bf16
+       * dims, one ue8m0 scale per 64 coded dims, one pad byte. The page gives the
+       * parts and the total only; they are taken in the order its sum lists them:
+       * bytes [0,448) codes of dims 0..447, [448,576) dims 448..511 as bf16,
+       * [576,583) scale byte g for dims 64g..64g+63, byte 583 unused. */
+      for (d = 0; d < 448; d++) k[d] = orc_e4m3(r[d]) * orc_ue8m0(r[576 + d / 64]);
+      for (d = 0; d < 64; d++) k[448 + d] = orc_bf16(r[448 + 2 * d] | (r[448 + 2 * d + 1] << 8));
       break;
     }
     case ORC_NVFP4_288: {

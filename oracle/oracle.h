@@ -28,7 +28,8 @@
 extern "C" {
 #endif
 
-enum { ORC_FP8_SLOTSCALE = 0, ORC_FP8_528 = 1, ORC_NVFP4_288 = 2, ORC_V32_656 = 3, ORC_FP8_UE8M0 = 4 };
+enum { ORC_FP8_SLOTSCALE = 0, ORC_FP8_528 = 1, ORC_NVFP4_288 = 2, ORC_V32_656 = 3, ORC_FP8_UE8M0 = 4,
+       ORC_MODEL1_584 = 5 };
 
 typedef struct {
   const uint8_t* base;     /* host bytes of page 0                                   */
@@ -51,7 +52,7 @@ double orc_e4m3(int code);          /* e4m3fn; 0x7F / 0xFF are NaN              
 double orc_e2m1(int nibble);        /* e2m1                                                */
 double orc_bf16(int bits);          /* bf16 bit pattern                                    */
 double orc_ue8m0(int byte);         /* 2^(byte - 127); 0xFF is NaN                         */
-int orc_record_bytes(int format);   /* 512, 528, 288, 656, 528; -1 if unknown              */
+int orc_record_bytes(int format);   /* 512, 528, 288, 656, 528, 584; -1 if unknown         */
 int orc_record_dims(int format);    /* d_qk of the format: 512 or 576                      */
 
 /* Decode slot `sid` into k[0..dims). Returns 1 if the slot is in range and was

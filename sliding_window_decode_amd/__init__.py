@@ -15,7 +15,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsda.so")
 
-FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656, FP8_UE8M0 = 0, 1, 2, 3, 4
+FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656, FP8_UE8M0, MODEL1_584 = 0, 1, 2, 3, 4, 5
 META_INTS = 8
 
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_HIP = 0, -1, -2, -3, -4

@@ -56,6 +56,10 @@ int check_cache(const sda_cache* c, int d_qk, const char* which) {
              sda_format_dims(c->format), d_qk);
     return fail(SDA_ERR_UNSUPPORTED, msg);
   }
+  if (c->format == SDA_MODEL1_584) {
+    snprintf(msg, sizeof(msg), "%s cache: format %d is not decoded yet", which, c->format);
+    return fail(SDA_ERR_UNSUPPORTED, msg);
+  }
   if (!aligned(c->base, 16)) return fail(SDA_ERR_INVALID_ARG, "cache base must be 16-byte aligned");
   if (c->num_pages < 1 || !is_pow2(c->page_size))
     return fail(SDA_ERR_INVALID_ARG, "cache needs num_pages >= 1 and a power-of-two page_size");
@@ -197,6 +201,7 @@ int sda_record_bytes(int format) {
     case SDA_NVFP4_288: return 288;
     case SDA_V32_656: return 656;
     case SDA_FP8_UE8M0: return 528;
+    case SDA_MODEL1_584: return 584;
     default: return -1;
   }
 }
@@ -206,7 +211,8 @@ int sda_format_dims(int format) {
     case SDA_FP8_SLOTSCALE:
     case SDA_FP8_528:
     case SDA_NVFP4_288:
-    case SDA_FP8_UE8M0: return 512;
+    case SDA_FP8_UE8M0:
+    case SDA_MODEL1_584: return 512;
     case SDA_V32_656: return 576;
     default: return -1;
   }

@@ -69,6 +69,20 @@ def decode_rows(cache, sids) -> np.ndarray:
             e = r[512:528].astype(np.float64)
             sc = np.where(e == 255, np.nan, np.exp2(e - 127.0))
             out.append(e4m3_torch(r[:512]) * np.repeat(sc, g))
+        elif cache.fmt == 5:  # MODEL1_584: the parts at the offsets of the stated part order
+            lay = L["model1_584"]
+            off, o = {}, 0
+            for name, n in lay["parts"].items():
+                off[name] = o
+                o += n
+            g = lay["scale_group_dims"]
+            a = off["e4m3_codes"]
+            e = r[off["ue8m0_scales"]:off["ue8m0_scales"] + lay["parts"]["ue8m0_scales"]].astype(np.float64)
+            sc = np.where(e == 255, np.nan, np.exp2(e - 127.0))
+            nope = e4m3_torch(r[a:a + lay["parts"]["e4m3_codes"]]) * np.repeat(sc, g)
+            b = off["bf16_rope"]
+            rope = bf16_torch(r[b:b + lay["parts"]["bf16_rope"]].copy().view(np.uint16))
+            out.append(np.concatenate([nope, rope]))
         elif cache.fmt == 2:  # NVFP4_288
             packed = r[:256]
             nib = np.empty(512, dtype=np.int64)

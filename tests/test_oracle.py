@@ -55,12 +55,16 @@ def test_record_sizes_match_pages(orc):
     assert L.orc_record_bytes(wl.FP8_SLOTSCALE) == g["fp8_slotscale_512"]["bytes"]
     assert L.orc_record_bytes(wl.FP8_UE8M0) == g["fp8_ue8m0_528"]["bytes"] == sum(g["fp8_ue8m0_528"]["parts"].values())
     assert L.orc_record_dims(wl.FP8_UE8M0) == 512
+    assert L.orc_record_bytes(wl.MODEL1_584) == g["model1_584"]["bytes"] == sum(g["model1_584"]["parts"].values())
+    assert L.orc_record_dims(wl.MODEL1_584) == 512
+    assert g["model1_584"]["parts"]["ue8m0_scales"] * g["model1_584"]["scale_group_dims"] == g["model1_584"]["parts"]["e4m3_codes"]
     assert L.orc_record_dims(wl.V32_656) == 576 and L.orc_record_dims(wl.FP8_528) == 512
     for f in wl.RECORD_BYTES:
         assert L.orc_record_bytes(f) == wl.RECORD_BYTES[f]
 
 
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0,
+                                 wl.MODEL1_584])
 @pytest.mark.parametrize("pad", [0, 96])
 def test_decode_slot_matches_library_decoding(orc, fmt, pad):
     rng = np.random.default_rng(fmt * 10 + pad)
@@ -110,6 +114,26 @@ def test_ue8m0_chunk_and_scale_mapping(orc):
     rec[32:48] = 0xB8                                     # chunk 2 (dims 32..47): e4m3 -1.0, scale byte 1
     k = orc.decode_slot(c, 0)
     assert np.all(k[16:32] == 2.0 * 2.0 ** -8) and np.all(k[32:48] == -(2.0 ** -7))
+
+
+def test_model1_parts_and_scale_mapping(orc):
+    """MODEL1 record: dims 0..447 are e4m3 codes times scale byte d // 64 of the 7 after the bf16 part,
+    dims 448..511 the bf16 values (no scale), the last byte plays no part."""
+    c = wl.make_cache(np.random.default_rng(0), wl.MODEL1_584, 64, page_size=64)
+    rec = c.data[:584]
+    rec[:448] = 0x38                                      # e4m3 1.0 in every coded dim
+    rec[576:583] = 124 + np.arange(7, dtype=np.uint8)     # scales 2^-3 .. 2^3
+    rope = np.linspace(-3, 3, 64).astype(np.float32)
+    rec[448:576] = wl.bf16_bits(rope).view(np.uint8)
+    k = orc.decode_slot(c, 0)
+    assert np.array_equal(k[:448], np.repeat(2.0 ** (np.arange(7) - 3), 64))
+    assert np.array_equal(k[448:], wl.bf16_round(rope).astype(np.float64))
+    rec[583] = 0xFF                                       # the pad byte
+    rec[63:65] = 0xB8                                     # dims 63 (scale 0) and 64 (scale 1): e4m3 -1.0
+    k2 = orc.decode_slot(c, 0)
+    assert k2[63] == -(2.0 ** -3) and k2[64] == -(2.0 ** -2)
+    k2[63:65] = k[63:65]
+    assert np.array_equal(k2, k)
 
 
 def test_ue8m0_equals_fp32_scales_when_a_group_shares_one(orc):
@@ -308,7 +332,8 @@ def test_lens_zero_gives_zero_output_and_sink_lse(orc):
     assert np.all(out == 0) and np.all(lse == -np.inf)
 
 
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0,
+                                 wl.MODEL1_584])
 def test_single_valid_slot_returns_its_row(orc, fmt):
     w = _w(6, fmt=fmt, width=8)
     w.lst.idx[:, :] = -1

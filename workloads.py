@@ -21,12 +21,17 @@ Record formats (bytes of one slot; ``page_stride`` bytes between pages):
 * ``FP8_UE8M0`` (528 B): 512 e4m3 codes, then 16 ue8m0 scale bytes, byte g the
   power-of-two scale 2^(g - 127) of dims 32g..32g+31 (vLLM swapab_decode_attn
   page, stage_inputs: fp8 chunk c of 16 dims takes scale byte c // 2).
+* ``MODEL1_584`` (584 B, d_qk = d_v = 512): 448 e4m3 codes (dims 0..447), 64 bf16
+  values (dims 448..511), 7 ue8m0 scale bytes (byte g scales dims 64g..64g+63),
+  one zero pad byte (FlashMLA sparse_decode.h page: the MODEL1 bytes-per-token
+  sum 448 + 64*2 + 448/64 + 1; the parts in the order of that sum).
 
 Quantization of the synthetic N(0,1) data: e4m3 by torch's float8_e4m3fn cast
 after clipping to +-448 (round-to-nearest-even with saturation); FP8_UE8M0 rows
 first get a random magnitude 2^U{-4..4} per 32-dim block, then each block the
 scale exponent ceil(log2(amax / 448)) (the MXFP8 rule of the vLLM page's output
-cast) and codes e4m3(x / scale); NVFP4 by the
+cast) and codes e4m3(x / scale); MODEL1_584 rows the same per 64-dim block of
+dims 0..447, dims 448..511 bf16(N(0,1)); NVFP4 by the
 usual recipe, block scale = e4m3(amax/6) and codes = round-to-nearest-even of
 x/scale on the e2m1 grid, saturating at 6 (torch has no float->e2m1 cast, so
 the grid rounding is written out here).
@@ -40,11 +45,11 @@ from typing import Optional
 import numpy as np
 import torch
 
-FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656, FP8_UE8M0 = 0, 1, 2, 3, 4
+FP8_SLOTSCALE, FP8_528, NVFP4_288, V32_656, FP8_UE8M0, MODEL1_584 = 0, 1, 2, 3, 4, 5
 FORMAT_NAMES = {FP8_SLOTSCALE: "fp8_slotscale", FP8_528: "fp8_528", NVFP4_288: "nvfp4_288", V32_656: "v32_656",
-                FP8_UE8M0: "fp8_ue8m0"}
-RECORD_BYTES = {FP8_SLOTSCALE: 512, FP8_528: 528, NVFP4_288: 288, V32_656: 656, FP8_UE8M0: 528}
-D_QK = {FP8_SLOTSCALE: 512, FP8_528: 512, NVFP4_288: 512, V32_656: 576, FP8_UE8M0: 512}
+                FP8_UE8M0: "fp8_ue8m0", MODEL1_584: "model1_584"}
+RECORD_BYTES = {FP8_SLOTSCALE: 512, FP8_528: 528, NVFP4_288: 288, V32_656: 656, FP8_UE8M0: 528, MODEL1_584: 584}
+D_QK = {FP8_SLOTSCALE: 512, FP8_528: 512, NVFP4_288: 512, V32_656: 576, FP8_UE8M0: 512, MODEL1_584: 512}
 
 
 @dataclasses.dataclass
@@ -115,17 +120,34 @@ def e4m3_codes(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def ue8m0_records(rng: np.random.Generator, x: np.ndarray) -> np.ndarray:
-    """[n, 512] float32 -> [n, 528] FP8_UE8M0 records: per 32-dim block a random magnitude 2^U{-4..4}, then
-    the block's scale byte 127 + ceil(log2(amax / 448)) (clamped to 1..254) and codes e4m3(x / scale)."""
-    n = x.shape[0]
-    blocks = x.reshape(n, 16, 32) * np.exp2(rng.integers(-4, 5, size=(n, 16, 1))).astype(np.float32)
+def _mx_blocks(rng: np.random.Generator, x: np.ndarray, block: int):
+    """[n, d] float32 -> (codes [n, d] uint8, scale bytes [n, d / block] uint8): per block a random magnitude
+    2^U{-4..4}, then the block's scale byte 127 + ceil(log2(amax / 448)) (clamped to 1..254) and codes
+    e4m3(x / scale)."""
+    n, d = x.shape
+    nb = d // block
+    blocks = x.reshape(n, nb, block) * np.exp2(rng.integers(-4, 5, size=(n, nb, 1))).astype(np.float32)
     amax = np.abs(blocks).max(axis=2)
     with np.errstate(divide="ignore"):
         ex = np.where(amax > 0, np.ceil(np.log2(amax / 448.0)), -127.0)
     ex = np.clip(ex, -126, 127).astype(np.int32)
-    codes = e4m3_codes((blocks / np.exp2(ex)[:, :, None].astype(np.float32)).reshape(n, 512))
-    return np.concatenate([codes, (ex + 127).astype(np.uint8)], axis=1)
+    codes = e4m3_codes((blocks / np.exp2(ex)[:, :, None].astype(np.float32)).reshape(n, d))
+    return codes, (ex + 127).astype(np.uint8)
+
+
+def ue8m0_records(rng: np.random.Generator, x: np.ndarray) -> np.ndarray:
+    """[n, 512] float32 -> [n, 528] FP8_UE8M0 records (one scale byte per 32 dims)."""
+    codes, sb = _mx_blocks(rng, x, 32)
+    return np.concatenate([codes, sb], axis=1)
+
+
+def model1_records(rng: np.random.Generator, x: np.ndarray) -> np.ndarray:
+    """[n, 512] float32 -> [n, 584] MODEL1_584 records: dims 0..447 as e4m3 with one scale byte per 64
+    dims, dims 448..511 replaced by bf16(N(0,1)), one zero pad byte."""
+    n = x.shape[0]
+    codes, sb = _mx_blocks(rng, x[:, :448], 64)
+    rope = bf16_bits(rng.standard_normal((n, 64), dtype=np.float32)).view(np.uint8).reshape(n, 128)
+    return np.concatenate([codes, rope, sb, np.zeros((n, 1), dtype=np.uint8)], axis=1)
 
 
 def e4m3_values(codes: np.ndarray) -> np.ndarray:
@@ -186,6 +208,9 @@ def make_cache(rng: np.random.Generator, fmt: int, num_slots: int, page_size: in
             continue
         if fmt == FP8_UE8M0:
             recs[s0:s0 + n] = ue8m0_records(rng, x)
+            continue
+        if fmt == MODEL1_584:
+            recs[s0:s0 + n] = model1_records(rng, x)
             continue
         recs[s0:s0 + n, :512] = e4m3_codes(x)
         if fmt in (FP8_528, V32_656):
