@@ -56,10 +56,6 @@ int check_cache(const sda_cache* c, int d_qk, const char* which) {
              sda_format_dims(c->format), d_qk);
     return fail(SDA_ERR_UNSUPPORTED, msg);
   }
-  if (c->format == SDA_MODEL1_584) {
-    snprintf(msg, sizeof(msg), "%s cache: format %d is not decoded yet", which, c->format);
-    return fail(SDA_ERR_UNSUPPORTED, msg);
-  }
   if (!aligned(c->base, 16)) return fail(SDA_ERR_INVALID_ARG, "cache base must be 16-byte aligned");
   if (c->num_pages < 1 || !is_pow2(c->page_size))
     return fail(SDA_ERR_INVALID_ARG, "cache needs num_pages >= 1 and a power-of-two page_size");
@@ -145,7 +141,9 @@ hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_gro
   const bool fp4 = p.lst[0].format == SDA_NVFP4_288 || (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288);
   // the ring kernel takes FP8_UE8M0 lists only when every list is one
   const int ue = (p.lst[0].format == SDA_FP8_UE8M0) + (p.nlists > 1 && p.lst[1].format == SDA_FP8_UE8M0);
-  const bool staged = fp4 || (ue > 0 && ue < p.nlists);
+  // MODEL1_584 rows hold bf16 value dims, which the register-staged kernel's bf16 tile takes as they are
+  const bool m1 = p.lst[0].format == SDA_MODEL1_584 || (p.nlists > 1 && p.lst[1].format == SDA_MODEL1_584);
+  const bool staged = fp4 || m1 || (ue > 0 && ue < p.nlists);
   // the register-staged kernel takes at most 32 heads per workgroup
   return staged ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision,
                                        stream)

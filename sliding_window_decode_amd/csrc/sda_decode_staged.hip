@@ -1,4 +1,4 @@
-// sda_decode_staged.hip -- split-KV decode attention for calls with an NVFP4 list, on gfx950: records
+// sda_decode_staged.hip -- split-KV decode attention for calls with an NVFP4 or MODEL1 list, on gfx950: records
 // staged through registers, widened into a bf16 tile in LDS.
 //
 // Workgroup = one scheduler part x a group of 16 or 32 query heads, 4 waves. Wave w owns output dims
@@ -111,9 +111,11 @@ void decode_kernel(DecodeParams p) {
     }
   };
 
-  // ---- record staging (registers): the sub-tile's data chunks, its scale chunk and rope chunk
+  // ---- record staging (registers): the sub-tile's data chunks, its scale chunk and bf16 chunk
+  // (MODEL1_584 rows: 28 code chunks, then 8 bf16 chunks for dims 448..511, loaded like the rope dims of
+  // d_qk 576 rows; the code loads of lanes 28..31 fall inside the record and are not used)
   u32x4 stg[4];
-  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; FP8_UE8M0: the word holding its ue8m0 byte
+  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; ue8m0 formats: the word holding its byte
   u32x4 stg_sc;
   u32x4 stg_rp;
   auto rec_issue = [&](const Item& it, int s) {
@@ -134,10 +136,14 @@ void decode_kernel(DecodeParams p) {
         const int r = (tid >> 5) + 8 * k, c = tid & 31;
         const uint64_t a = sm.addr[s][r];
         stg[k] = ld_global_16(a ? a + 16 * c : dummy);
-        // chunk c (dims 16c .. 16c+15) takes scale byte c / 2: byte (c / 2) % 4 of word c / 8
+        // FP8_UE8M0: chunk c (dims 16c .. 16c+15) takes scale byte c / 2: byte (c / 2) % 4 of word c / 8.
+        // MODEL1_584: scale byte c / 4 (64 dims each) of the 7 at byte 576: byte (c / 4) % 4 of word c / 16
         if (ld.format == SDA_FP8_UE8M0) stg_sb[k] = *(gbl_u32*)(a ? a + 512 + 4 * (c >> 3) : dummy);
+        if constexpr (!kRope) {
+          if (ld.format == SDA_MODEL1_584) stg_sb[k] = *(gbl_u32*)(a ? a + 576 + 4 * (c >> 4) : dummy);
+        }
       }
-      if (tid < KT && ld.format != SDA_FP8_UE8M0) {
+      if (tid < KT && ld.format != SDA_FP8_UE8M0 && ld.format != SDA_MODEL1_584) {
         const uint64_t sa = sm.saddr[s][tid];
         if (ld.format == SDA_FP8_SLOTSCALE)
           stg_sc[0] = *(gbl_u32*)(sa ? sa : dummy);
@@ -147,6 +153,9 @@ void decode_kernel(DecodeParams p) {
       if constexpr (kRope) {
         const uint64_t a = sm.addr[s][tid >> 3];
         stg_rp = ld_global_16(a ? a + 528 + 16 * (tid & 7) : dummy);
+      } else if (ld.format == SDA_MODEL1_584) {
+        const uint64_t a = sm.addr[s][tid >> 3];
+        stg_rp = ld_global_16(a ? a + 448 + 16 * (tid & 7) : dummy);
       }
     }
   };
@@ -182,6 +191,7 @@ void decode_kernel(DecodeParams p) {
       }
     } else {
       const bool ue8m0 = ld.format == SDA_FP8_UE8M0;
+      const bool m1 = !kRope && ld.format == SDA_MODEL1_584;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int r = (tid >> 5) + 8 * k, c = tid & 31;
@@ -189,7 +199,9 @@ void decode_kernel(DecodeParams p) {
         const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
         // ue8m0 records: the power-of-two scale is applied by the conversion (the row's scale table
         // then holds 1); other formats convert unscaled
-        const float cs = ue8m0 ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 1) & 3))) : 1.0f;
+        const float cs = ue8m0 ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 1) & 3)))
+                         : m1  ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 2) & 3)))
+                               : 1.0f;
         uint32_t y[8];
         e4m3x4_to_bf16_scaled(x[0], cs, y[0], y[1]);
         e4m3x4_to_bf16_scaled(x[1], cs, y[2], y[3]);
@@ -198,8 +210,10 @@ void decode_kernel(DecodeParams p) {
         const int f = ((r & 3) << 1) | ((r >> 2) & 1);
         char* row = sm.tile + r * RS;
         const int c0 = 2 * c, c1 = 2 * c + 1;
-        *(u32x4*)(row + 16 * ((c0 & ~7) | ((c0 ^ f) & 7))) = u32x4{y[0], y[1], y[2], y[3]};
-        *(u32x4*)(row + 16 * ((c1 & ~7) | ((c1 ^ f) & 7))) = u32x4{y[4], y[5], y[6], y[7]};
+        if (!m1 || c < 28) {  // MODEL1_584: bf16 chunks 56..63 come from the bf16 part below
+          *(u32x4*)(row + 16 * ((c0 & ~7) | ((c0 ^ f) & 7))) = u32x4{y[0], y[1], y[2], y[3]};
+          *(u32x4*)(row + 16 * ((c1 & ~7) | ((c1 ^ f) & 7))) = u32x4{y[4], y[5], y[6], y[7]};
+        }
       }
       if (tid < KT) {
         const bool ok = sm.addr[s][tid] != 0;
@@ -207,7 +221,7 @@ void decode_kernel(DecodeParams p) {
         if (ld.format == SDA_FP8_SLOTSCALE) {
           const float v = __builtin_bit_cast(float, stg_sc[0]);
           sc = f32x4{v, v, v, v};
-        } else if (ue8m0) {
+        } else if (ue8m0 || m1) {
           sc = f32x4{1.f, 1.f, 1.f, 1.f};
         } else {
           sc = __builtin_bit_cast(f32x4, stg_sc);
@@ -216,6 +230,11 @@ void decode_kernel(DecodeParams p) {
       }
       if constexpr (kRope) {
         const int r = tid >> 3, c = 64 + (tid & 7);
+        const bool ok = sm.addr[s][r] != 0;
+        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        *(u32x4*)(sm.tile + r * RS + 16 * ((c & ~7) | ((c ^ f) & 7))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};
+      } else if (m1) {
+        const int r = tid >> 3, c = 56 + (tid & 7);
         const bool ok = sm.addr[s][r] != 0;
         const int f = ((r & 3) << 1) | ((r >> 2) & 1);
         *(u32x4*)(sm.tile + r * RS + 16 * ((c & ~7) | ((c ^ f) & 7))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};

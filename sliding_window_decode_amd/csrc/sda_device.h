@@ -26,7 +26,10 @@ typedef const __attribute__((address_space(1))) u32x4 gbl_u32x4;
 typedef const __attribute__((address_space(1))) uint32_t gbl_u32;
 typedef const __attribute__((address_space(1))) uint16_t gbl_u16;
 
-__device__ __forceinline__ u32x4 ld_global_16(uint64_t addr) { return *(gbl_u32x4*)addr; }
+// 16 bytes from an 8-byte aligned address (records of 584 bytes start 8-byte aligned; the load is
+// the same global_load_dwordx4 as for a 16-byte aligned one)
+typedef const __attribute__((address_space(1))) u32x4 __attribute__((aligned(8))) gbl_u32x4_a8;
+__device__ __forceinline__ u32x4 ld_global_16(uint64_t addr) { return *(gbl_u32x4_a8*)addr; }
 __device__ __forceinline__ uint32_t ld_global_u16(uint64_t addr) { return *(gbl_u16*)addr; }
 
 // Exact e4m3fn -> bf16 of the 4 codes of a word (the gfx950 conversion decodes the OCP format; every

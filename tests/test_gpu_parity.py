@@ -26,7 +26,7 @@ def _log(msg):
 
 
 SMALL_T = {"c1_tiny_swa": 4, "c2_swa_h128": 6, "c3_swa_fp8extra": 12, "c4_swa_nvfp4extra": 6, "c5_topk_v32": 3,
-           "c6_swa_ue8m0": 12}
+           "c6_swa_ue8m0": 12, "c7_swa_model1": 12}
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -91,6 +91,44 @@ def test_ue8m0_lists(fmt, xfmt, H, precision):
             count_flips=precision > 1)
 
 
+# MODEL1_584 lists (448 fp8 dims with a power-of-two scale per 64, 64 bf16 dims that are values too) run
+# the staged kernel, alone or with a list of any other 512-dim format
+@pytest.mark.parametrize("fmt,xfmt", [(wl.MODEL1_584, wl.MODEL1_584), (wl.MODEL1_584, None),
+                                      (wl.MODEL1_584, wl.NVFP4_288), (wl.FP8_528, wl.MODEL1_584),
+                                      (wl.FP8_UE8M0, wl.MODEL1_584), (wl.MODEL1_584, wl.FP8_SLOTSCALE)])
+@pytest.mark.parametrize("H,precision", [(16, 2), (32, 3), (64, 2), (128, 2)])
+def test_model1_lists(fmt, xfmt, H, precision):
+    w = wl.small_workload(90 + 7 * fmt + (xfmt or 0) + H, fmt, xfmt, T=9, H=H, width=140,
+                          xwidth=300 if xfmt is not None else 0, num_slots=2048, sink=True, p_invalid=0.05,
+                          page_size=16)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0)
+    plan.precision = precision
+    out, lse, dec = DeviceWorkload(w).run(plan=plan)
+    compare(out, lse, o_ref, l_ref, what=f"model1 {fmt}/{xfmt} H={H} precision {precision}",
+            count_flips=precision > 1)
+
+
+def test_model1_bf16_dims_are_values():
+    """A single valid MODEL1 row: the output is the row itself, its bf16 dims 448..511 included, exactly;
+    the pad byte changes nothing."""
+    rng = np.random.default_rng(8)
+    c = wl.make_cache(rng, wl.MODEL1_584, 64, page_size=16)
+    q = wl.make_q(rng, 3, 16, 512)
+    idx = np.full((3, 40), -1, dtype=np.int32)
+    idx[np.arange(3), [0, 17, 39]] = [5, 16, 63]
+    lst = wl.SlotList(idx, 40, np.full(3, 40, dtype=np.int32))
+    w = wl.Workload("model1 rows", 3, 16, 512, 512, q, c, lst, None, None, None, 0.05)
+    _, out, _ = _run_cmp(w, "model1 rows")
+    pages = c.data.reshape(c.num_pages, c.page_stride)
+    pages[:, 583::584][:, :16] = 0xFF
+    _, out2, _ = _run_cmp(w, "model1 rows, pad set")
+    assert torch.equal(out, out2)
+    for t, s in enumerate([5, 16, 63]):
+        ref = oracle.decode_slot(c, s)
+        assert np.array_equal(out[t, 0].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
+
+
 # 64-head workgroups (eight waves with 32 rows and 256 dims each) for every fp8 record layout; a call
 # with an NVFP4 list runs 32-head workgroups under the same plan
 @pytest.mark.parametrize("fmt,xfmt,H", [(wl.FP8_SLOTSCALE, None, 64), (wl.FP8_528, wl.FP8_528, 128),
@@ -107,7 +145,8 @@ def test_64_head_workgroups(fmt, xfmt, H, parts):
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0,
+                                 wl.MODEL1_584])
 def test_heads_and_formats(H, fmt):
     w = wl.small_workload(10 + H + fmt, fmt, None, T=3, H=H, width=200, num_slots=1024, sink=(H % 32 == 0),
                           p_invalid=0.1, lens_lo=0)
@@ -151,7 +190,8 @@ def test_all_slots_invalid():
     _run_cmp(w, "all -1")
 
 
-@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656])
+@pytest.mark.parametrize("fmt", [wl.FP8_SLOTSCALE, wl.FP8_528, wl.NVFP4_288, wl.V32_656, wl.FP8_UE8M0,
+                                 wl.MODEL1_584])
 def test_single_valid_slot_returns_its_row(fmt):
     w = wl.small_workload(52 + fmt, fmt, None, T=4, H=32, width=100, num_slots=512)
     w.lst.idx[:] = -1

@@ -256,7 +256,8 @@ def make_sink(rng: np.random.Generator, H: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- the five configurations
 
-CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32", "c6_swa_ue8m0")
+CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32", "c6_swa_ue8m0",
+           "c7_swa_model1")
 
 
 def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Workload:
@@ -273,6 +274,8 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
                      V32_656 cache; lens = 2048; sink; scale 1/sqrt(576).
     c6_swa_ue8m0     c3's shape with both caches in FP8_UE8M0 (the fp8 record with one power-of-two
                      scale per 32 dims); a measurement workload for that format, not one of the five.
+    c7_swa_model1    c3's shape with both caches in MODEL1_584 (448 fp8 dims with a power-of-two scale
+                     per 64 dims, 64 bf16 dims); a measurement workload for that format.
     All pages hold 64 slots.
     """
     rng = np.random.default_rng(seed)
@@ -325,6 +328,16 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
         q = make_q(rng, T, H, 512)
         cache = make_cache(rng, FP8_UE8M0, 32768, 64, pad)
         xcache = make_cache(rng, FP8_UE8M0, 65536, 64, pad)
+        lst = make_list(rng, T, 128, 32768, 1, 128)
+        xlst = make_list(rng, T, 512, 65536, 1, 512)
+        sink = make_sink(rng, H)
+        return Workload(name, T, H, 512, 512, q, cache, lst, xcache, xlst, sink, float(np.float32(1 / math.sqrt(512))))
+    if name == "c7_swa_model1":
+        T = 256 if T is None else T
+        H = 32
+        q = make_q(rng, T, H, 512)
+        cache = make_cache(rng, MODEL1_584, 32768, 64, pad)
+        xcache = make_cache(rng, MODEL1_584, 65536, 64, pad)
         lst = make_list(rng, T, 128, 32768, 1, 128)
         xlst = make_list(rng, T, 512, 65536, 1, 512)
         sink = make_sink(rng, H)
