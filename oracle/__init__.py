@@ -61,6 +61,12 @@ def lib():
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.orc_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_rope_q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_mxfp8_out.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -131,6 +137,48 @@ def attention(w, tokens: Optional[slice] = None, nthreads: int = 1, sink="defaul
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, lse
+
+
+def rope_q(q: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray) -> np.ndarray:
+    """q bf16 bits [T, H, 512] with dims 448..511 rotated by the positions' angles (bf16 bits, same shape)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    T, H, d = q.shape
+    assert d == 512
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.float32)
+    out = np.empty_like(q)
+    lib().orc_rope_q(q.ctypes.data, H * d, d, T, H, pos.ctypes.data, cs.ctypes.data, cs.shape[1], cs.shape[0],
+                     out.ctypes.data)
+    return out
+
+
+def mxfp8_out(out: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray):
+    """Inverse RoPE and MXFP8 cast of attention results out [T, H, 512] (float64): (codes uint8 [T, H, 512],
+    scale bytes uint8 [T, H, 16])."""
+    o = np.ascontiguousarray(out, dtype=np.float64)
+    T, H, d = o.shape
+    assert d == 512
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.float32)
+    codes = np.empty((T, H, 512), dtype=np.uint8)
+    scales = np.empty((T, H, 16), dtype=np.uint8)
+    lib().orc_mxfp8_out(o.ctypes.data, T, H, pos.ctypes.data, cs.ctypes.data, cs.shape[1], cs.shape[0],
+                        codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def attention_v41(w, tokens: Optional[slice] = None, nthreads: int = 1):
+    """The V4.1 decode of workload `w` (which carries `rope`): Q RoPE, attention, inverse RoPE and the MXFP8
+    output cast. Returns (codes [T, H, 512], scale bytes [T, H, 16], lse [T, H], out [T, H, 512] float64 before
+    the cast) for all tokens or a slice of them."""
+    import copy
+    assert w.rope is not None and w.d_qk == 512
+    w2 = copy.copy(w)
+    w2.q = rope_q(w.q, w.rope.positions, w.rope.cos_sin)
+    out, lse = attention(w2, tokens=tokens, nthreads=nthreads)
+    pos = w.rope.positions if tokens is None else w.rope.positions[tokens]
+    codes, scales = mxfp8_out(out, pos, w.rope.cos_sin)
+    return codes, scales, lse, out
 
 
 def merge(o_parts: np.ndarray, lse_parts: np.ndarray, sink: Optional[np.ndarray]):

@@ -291,3 +291,123 @@ void orc_merge(int n, int H, int d_v, const double* o, const double* part_lse, c
     lse[h] = M + log(den);
   }
 }
+
+/* ------------------------------------------------- V4.1 prologue / epilogue */
+
+#define ORC_ROPE_START 448
+#define ORC_ROPE_PAIRS 32
+
+static float f32_of_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round to nearest even on the 16 dropped bits: add 0x7FFF plus the lowest kept
+ * bit, then truncate (a carry into the exponent is the correct rounding up). */
+int orc_bf16_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (int)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (int)(u >> 16);
+}
+
+/* e4m3fn values are m/8 * 2^-6 (subnormal, code m) and (1 + m/8) * 2^(e-7)
+ * (code 8e + m); the codes of non-negative values are monotone in the value,
+ * so rounding the value to the nearest multiple of its binade's step and
+ * counting steps gives the code. */
+int orc_e4m3_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  int sign = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  int code;
+  if (a < ldexp(1.0, -6)) {
+    code = (int)nearbyint(ldexp(a, 9));          /* steps of 2^-9; 8 steps is the first normal */
+  } else {
+    int e;
+    frexp(a, &e);                                /* a = f * 2^e, f in [0.5, 1)                   */
+    int be = e - 1;                              /* a in [2^be, 2^(be+1))                        */
+    int m = (int)nearbyint(ldexp(a, 3 - be)) - 8; /* eighths above 1; 8 carries into the binade  */
+    code = 8 * (be + 7) + m;
+  }
+  if (code > 0x7E) code = 0x7E;
+  return sign | code;
+}
+
+static void cos_sin_of(const float* cs, int64_t stride, int64_t npos, int64_t pos, int i, float* c, float* s) {
+  if (pos < 0 || pos >= npos) {
+    *c = 1.0f;
+    *s = 0.0f;
+    return;
+  }
+  *c = cs[pos * stride + i];
+  *s = cs[pos * stride + ORC_ROPE_PAIRS + i];
+}
+
+void orc_rope_q(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
+                const int64_t* positions, const float* cos_sin, int64_t cs_stride, int64_t num_positions,
+                uint16_t* q_out) {
+  int t, h, d, i;
+  for (t = 0; t < T; t++) {
+    for (h = 0; h < H; h++) {
+      const uint16_t* src = q + (int64_t)t * q_stride_t + (int64_t)h * q_stride_h;
+      uint16_t* dst = q_out + ((int64_t)t * H + h) * 512;
+      for (d = 0; d < 512; d++) dst[d] = src[d];
+      for (i = 0; i < ORC_ROPE_PAIRS; i++) {
+        float c, s;
+        cos_sin_of(cos_sin, cs_stride, num_positions, positions[t], i, &c, &s);
+        int e = ORC_ROPE_START + 2 * i;
+        float qe = f32_of_bf16(src[e]), qo = f32_of_bf16(src[e + 1]);
+        float re = fmaf(qe, c, -(qo * s));
+        float ro = fmaf(qo, c, qe * s);
+        dst[e] = (uint16_t)orc_bf16_rne(re);
+        dst[e + 1] = (uint16_t)orc_bf16_rne(ro);
+      }
+    }
+  }
+}
+
+/* ue8m0 of y rounded up to a power of two: the biased exponent, plus one when
+ * any mantissa bit is set (y normal and positive here). */
+static int ue8m0_round_up(float y) {
+  uint32_t u;
+  memcpy(&u, &y, 4);
+  int e = (int)((u >> 23) & 0xFFu);
+  return e + ((u & 0x7FFFFFu) != 0u ? 1 : 0);
+}
+
+void orc_mxfp8_out(const double* out, int T, int H, const int64_t* positions, const float* cos_sin,
+                   int64_t cs_stride, int64_t num_positions, uint8_t* codes, uint8_t* scales) {
+  int t, h, d, i, k;
+  float x[512];
+  for (t = 0; t < T; t++) {
+    for (h = 0; h < H; h++) {
+      const double* o = out + ((int64_t)t * H + h) * 512;
+      for (d = 0; d < 512; d++) x[d] = (float)o[d];
+      for (i = 0; i < ORC_ROPE_PAIRS; i++) {
+        float c, s;
+        cos_sin_of(cos_sin, cs_stride, num_positions, positions[t], i, &c, &s);
+        int e = ORC_ROPE_START + 2 * i;
+        float oe = x[e], oo = x[e + 1];
+        x[e] = fmaf(oe, c, s * oo);
+        x[e + 1] = fmaf(oo, c, -(s * oe));
+      }
+      uint8_t* cd = codes + ((int64_t)t * H + h) * 512;
+      uint8_t* sc = scales + ((int64_t)t * H + h) * 16;
+      for (k = 0; k < 16; k++) {
+        float amax = 0.0f;
+        for (d = 32 * k; d < 32 * k + 32; d++) amax = fmaxf(amax, fabsf(x[d]));
+        amax = fmaxf(amax, 1e-10f);
+        int ex = ue8m0_round_up(amax * (float)(1.0 / 448.0));
+        uint32_t ib = (uint32_t)(254 - ex) << 23;
+        float inv;
+        memcpy(&inv, &ib, 4);
+        sc[k] = (uint8_t)ex;
+        for (d = 32 * k; d < 32 * k + 32; d++) cd[d] = (uint8_t)orc_e4m3_encode(x[d] * inv);
+      }
+    }
+  }
+}

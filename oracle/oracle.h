@@ -66,6 +66,32 @@ int orc_attn(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, i
              const orc_cache* cache, const orc_list* list, const orc_cache* xcache, const orc_list* xlist,
              const float* sink, float scale, double* out, double* lse, int nthreads);
 
+/* ---- V4.1 decode prologue and epilogue (vLLM swapab_decode_attn page: Q RoPE
+ * in stage_inputs, inverse RoPE and the MXFP8 output cast in device kernel step
+ * 9). Both follow the page's single-precision steps, so that the quantized
+ * results are decided in the precision the page takes them in.
+ * RoPE covers dims [448, 512) as 32 GPT-J pairs (dims 448 + 2i, 449 + 2i);
+ * cos_sin row p holds cos of pair i at [i] and its sin at [32 + i]. A position
+ * outside [0, num_positions) rotates nothing (cos 1, sin 0). */
+
+/* fp32 -> bf16 bits, round to nearest even (NaN stays NaN). */
+int orc_bf16_rne(float x);
+/* fp32 -> e4m3fn code, round to nearest even, saturating at +-448 (NaN -> 0x7F). */
+int orc_e4m3_encode(float x);
+/* q_out[t][h][d] (bf16 bits, [T][H][512] contiguous): q with its dims 448..511
+ * rotated by the angle of positions[t]: per pair, in fp32,
+ *   e' = fma(e, cos, -(o * sin)),  o' = fma(o, cos, e * sin),  rounded to bf16. */
+void orc_rope_q(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
+                const int64_t* positions, const float* cos_sin, int64_t cs_stride, int64_t num_positions,
+                uint16_t* q_out);
+/* MXFP8 output of attention results out [T][H][512] (taken to fp32 first): dims
+ * 448..511 rotated back per pair (e' = fma(e, cos, sin * o), o' = fma(o, cos,
+ * -(sin * e))), then per 32-dim chunk: amax = max(max |x|, 1e-10), scale byte =
+ * the ue8m0 of amax * (1/448) rounded up to a power of two, codes =
+ * e4m3(x * 2^(127 - byte)). codes: [T][H][512], scales: [T][H][16]. */
+void orc_mxfp8_out(const double* out, int T, int H, const int64_t* positions, const float* cos_sin,
+                   int64_t cs_stride, int64_t num_positions, uint8_t* codes, uint8_t* scales);
+
 /* LSE merge of n normalized partial results of one (token, head) group:
  * o: [n][H][d_v], part_lse: [n][H] (a part with no rows has lse -inf and is ignored).
  * The sink (may be NULL) enters the denominator once. out: [H][d_v], lse: [H]. */

@@ -502,3 +502,123 @@ def test_oracle_rejects_inconsistent_arguments(orc):
     w.d_qk = 576
     with pytest.raises(ValueError):
         orc.attention(w)
+
+
+# ------------------------------------------------------------------ V4.1 prologue and epilogue
+
+def test_bf16_encoder_matches_torch(orc):
+    L = orc.lib()
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.standard_normal(3000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 3000),
+                        # exact ties between two bf16 values (odd and even lower neighbours)
+                        (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38], dtype=np.float32)]).astype(np.float32)
+    got = np.array([L.orc_bf16_rne(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, wl.bf16_bits(x))
+
+
+def test_e4m3_encoder_matches_torch(orc):
+    L = orc.lib()
+    vals = e4m3_torch(np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8))
+    vals = np.unique(vals)
+    mids = (vals[1:] + vals[:-1]) / 2                    # ties: round to the even code
+    rng = np.random.default_rng(41)
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+                        rng.uniform(-460, 460, 4000), rng.standard_normal(2000) * 1e-3]).astype(np.float32)
+    got = np.array([L.orc_e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    ref = wl.e4m3_codes(x)
+    assert np.array_equal(got, ref)
+    # beyond the largest value the cast saturates (the page's MXFP8 scale keeps |x| <= 448 up to rounding)
+    for v in (448.5, 463.0, 1e6, np.inf):
+        assert L.orc_e4m3_encode(v) == 0x7E and L.orc_e4m3_encode(-v) == 0xFE
+    assert L.orc_e4m3_encode(float("nan")) == 0x7F
+
+
+def _rotate(x, cos, sin, sign=1.0):
+    """GPT-J pairs (2i, 2i+1) of x[..., 448:512] as complex numbers times exp(sign * i * angle), in float64."""
+    z = x[..., 448:512:2] + 1j * x[..., 449:512:2]
+    z = z * (cos + 1j * sign * sin)
+    y = x.copy()
+    y[..., 448:512:2] = z.real
+    y[..., 449:512:2] = z.imag
+    return y
+
+
+def test_rope_q_is_the_rotation_of_gptj_pairs(orc):
+    rng = np.random.default_rng(42)
+    T, H = 6, 4
+    q = wl.make_q(rng, T, H, 512)
+    rope = wl.make_rope(rng, T, num_positions=512)
+    rope.positions[0] = 0                                   # angle 0: identity
+    rope.positions[1] = 512                                 # outside the table: identity
+    rope.positions[2] = -1
+    got = bf16_torch(orc.rope_q(q, rope.positions, rope.cos_sin))
+    qf = bf16_torch(q)
+    assert np.array_equal(got[:3], qf[:3])
+    assert np.array_equal(got[:, :, :448], qf[:, :, :448])
+    cs = rope.cos_sin[rope.positions[3:]].astype(np.float64)
+    ref = _rotate(qf[3:], cs[:, None, :32], cs[:, None, 32:])
+    ref_b = bf16_torch(wl.bf16_bits(ref.astype(np.float32)))
+    # fp32 products and fma against the float64 rotation: equal after the bf16 rounding except where the
+    # exact value sits within fp32 rounding of a bf16 midpoint (then one bf16 step)
+    d = np.abs(got[3:] - ref_b)
+    ulp = np.abs(ref_b) * 2.0 ** -7 + 1e-30
+    assert np.all(d <= ulp)
+    assert (d > 0).mean() < 1e-3
+
+
+def test_mxfp8_scale_and_codes_closed_forms(orc):
+    T, H = 1, 1
+    pos = np.array([-1], dtype=np.int64)                    # identity rotation
+    cs = np.zeros((1, 64), dtype=np.float32)
+    out = np.zeros((T, H, 512))
+    out[0, 0, 0:32] = 1.0                                   # amax 1: smallest 2^e >= 1/448 is 2^-8 -> byte 119
+    out[0, 0, 32:64] = 448.0 * 2.0 ** -5                    # amax 448 * 2^k: scale exactly 2^k
+    out[0, 0, 64] = 448.0 * 2.0 ** -5                       # ... and one step above it: scale 2^(k+1)
+    out[0, 0, 65] = np.nextafter(np.float32(448.0 * 2.0 ** -5), np.float32(1e9))
+    out[0, 0, 96:128] = np.linspace(-3, 3, 32)
+    codes, sc = orc.mxfp8_out(out, pos, cs)
+    assert sc[0, 0, 0] == 119 and np.all(codes[0, 0, 0:32] == 0x78)        # 1 * 2^8 = 256 = 0x78
+    assert sc[0, 0, 1] == 127 - 5 and np.all(codes[0, 0, 32:64] == 0x7E)  # 448
+    assert sc[0, 0, 2] == 127 - 4 and codes[0, 0, 64] == 0x76              # 224
+    # all-zero chunks: amax is taken as 1e-10, codes 0
+    assert np.all(codes[0, 0, 128:] == 0) and sc[0, 0, 5] == sc[0, 0, 15]
+    e = sc[0, 0, 3].astype(np.float64) - 127
+    assert 3.0 / 448 <= 2.0 ** e < 2 * 3.0 / 448
+    np.testing.assert_allclose(e4m3_torch(codes[0, 0, 96:128]) * 2.0 ** e, out[0, 0, 96:128], rtol=2 ** -4)
+
+
+def test_mxfp8_out_undoes_the_rotation_and_bounds_the_error(orc):
+    """Results whose rope dims are u rotated by the position's angle come back as u (inverse RoPE), and every
+    decoded value is within half an e4m3 step of the unrounded one; the scale is the smallest power of two
+    that keeps the chunk within 448."""
+    rng = np.random.default_rng(43)
+    T, H = 5, 3
+    rope = wl.make_rope(rng, T, num_positions=1000)
+    u = rng.standard_normal((T, H, 512)) * 2.0 ** rng.integers(-6, 6, size=(T, H, 16)).repeat(32, axis=2)
+    cs = rope.cos_sin[rope.positions].astype(np.float64)
+    out = _rotate(u, cs[:, None, :32], cs[:, None, 32:])
+    codes, sc = orc.mxfp8_out(out, rope.positions, rope.cos_sin)
+    scale = 2.0 ** (sc.astype(np.float64) - 127)
+    dec = e4m3_torch(codes.reshape(-1)).reshape(codes.shape) * scale.repeat(32, axis=2)
+    amax = np.abs(u).reshape(T, H, 16, 32).max(axis=3)
+    assert np.all(amax <= 448 * scale * (1 + 1e-6)) and np.all(amax > 224 * scale * (1 - 1e-6))
+    # half a step of the value's binade (subnormal step below 2^-6), plus fp32 rounding of the rotation
+    x = u / scale.repeat(32, axis=2)
+    step = np.where(np.abs(x) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-300))) - 3))
+    err = np.abs(dec - u) / scale.repeat(32, axis=2)
+    assert np.all(err <= step / 2 + np.abs(x) * 1e-6 + 1e-12)
+
+
+def test_v41_with_identity_rotation_is_the_plain_decode_cast(orc):
+    w = _w(44, fmt=wl.FP8_UE8M0, xfmt=wl.FP8_UE8M0, sink=True, T=5)
+    w.rope = wl.make_rope(np.random.default_rng(1), w.T, num_positions=64)
+    w.rope.positions[:] = 64                                   # outside the table
+    codes, sc, lse, out = orc.attention_v41(w)
+    o, l = orc.attention(w)
+    assert np.array_equal(out, o) and np.array_equal(lse, l)
+    c2, s2 = orc.mxfp8_out(o, w.rope.positions, w.rope.cos_sin)
+    assert np.array_equal(codes, c2) and np.array_equal(sc, s2)
+    w.rope.positions[:] = 7
+    codes3, _, lse3, _ = orc.attention_v41(w)
+    assert not np.array_equal(lse3, l)                         # the rotation reaches the scores

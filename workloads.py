@@ -92,12 +92,29 @@ class Workload:
     xlst: Optional[SlotList]
     sink: Optional[np.ndarray]  # float32 [H] or None
     scale: float                # fp32 value
+    rope: Optional["Rope"] = None   # V4.1 decode: Q RoPE, inverse RoPE and MXFP8 output
 
     def lists(self):
         out = [(self.cache, self.lst)]
         if self.xcache is not None:
             out.append((self.xcache, self.xlst))
         return out
+
+
+@dataclasses.dataclass
+class Rope:
+    positions: np.ndarray       # int64 [T]: each token's position
+    cos_sin: np.ndarray         # float32 [num_positions, 64]: row p = cos(p th_i) for i < 32, then sin(p th_i)
+
+
+def make_rope(rng: np.random.Generator, T: int, num_positions: int = 8192, base: float = 10000.0) -> Rope:
+    """Positions U{0..num_positions-1} and the usual RoPE table over 32 pairs, th_i = base^(-i/32), computed in
+    float64 and stored as float32."""
+    pos = rng.integers(0, num_positions, size=T).astype(np.int64)
+    th = base ** (-np.arange(32, dtype=np.float64) / 32.0)
+    ang = np.arange(num_positions, dtype=np.float64)[:, None] * th[None, :]
+    cs = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return Rope(pos, cs)
 
 
 # ----------------------------------------------------------------------------- quantizers
@@ -257,7 +274,7 @@ def make_sink(rng: np.random.Generator, H: int) -> np.ndarray:
 # ----------------------------------------------------------------------------- the five configurations
 
 CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32", "c6_swa_ue8m0",
-           "c7_swa_model1")
+           "c7_swa_model1", "c8_v41_ue8m0")
 
 
 def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Workload:
@@ -276,6 +293,8 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
                      scale per 32 dims); a measurement workload for that format, not one of the five.
     c7_swa_model1    c3's shape with both caches in MODEL1_584 (448 fp8 dims with a power-of-two scale
                      per 64 dims, 64 bf16 dims); a measurement workload for that format.
+    c8_v41_ue8m0     c6 (same draws) as the full V4.1 decode call: positions U{0..8191} and a RoPE table,
+                     Q RoPE on dims 448..511, inverse RoPE and MXFP8 output.
     All pages hold 64 slots.
     """
     rng = np.random.default_rng(seed)
@@ -332,6 +351,11 @@ def make_workload(name: str, seed: int = 0, T: Optional[int] = None, **kw) -> Wo
         xlst = make_list(rng, T, 512, 65536, 1, 512)
         sink = make_sink(rng, H)
         return Workload(name, T, H, 512, 512, q, cache, lst, xcache, xlst, sink, float(np.float32(1 / math.sqrt(512))))
+    if name == "c8_v41_ue8m0":
+        w = make_workload("c6_swa_ue8m0", seed=seed, T=T, **kw)
+        w.name = name
+        w.rope = make_rope(np.random.default_rng([seed, 8]), w.T)
+        return w
     if name == "c7_swa_model1":
         T = 256 if T is None else T
         H = 32
