@@ -30,7 +30,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
                for f in ("sda_decode_ring.hip", "sda_decode_staged.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
-                         "sda_internal.h")]
+                         "sda_internal.h", "sda_v41.hip")]
 CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
 
 
@@ -40,10 +40,13 @@ def log(*a):
 
 def algorithmic_work(w):
     """Bytes and FLOPs the method needs: Q, the valid rows' records (+ the fp32 slot scale), the list
-    entries read (positions below the length), out and lse. Masked rows, padding and split partials
-    are not counted."""
+    entries read (positions below the length), out and lse (V4.1: fp8 out with its scale bytes, plus each
+    token's position and cos/sin row). Masked rows, padding and split partials are not counted."""
     rows = 0
-    byts = w.T * w.H * w.d_qk * 2 + w.T * w.H * w.d_v * 2 + w.T * w.H * 4
+    if getattr(w, "rope", None) is not None:
+        byts = w.T * w.H * w.d_qk * 2 + w.T * w.H * (w.d_v + w.d_v // 32) + w.T * w.H * 4 + w.T * (8 + 64 * 4)
+    else:
+        byts = w.T * w.H * w.d_qk * 2 + w.T * w.H * w.d_v * 2 + w.T * w.H * 4
     for cache, L in w.lists():
         qpl = max(1, getattr(L, "queries_per_len", 1))
         n = np.clip(L.lens[np.arange(w.T) // qpl], 0, L.width) if L.lens is not None else np.full(w.T, L.width)
@@ -202,10 +205,20 @@ def main():
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    v41 = w.rope is not None
+    if v41:
+        out8 = torch.empty((w.T, w.H, 512), dtype=torch.uint8, device="cuda")
+        osc = torch.empty((w.T, w.H, 16), dtype=torch.uint8, device="cuda")
+
     def step():
         dec.schedule(dw.lst, dw.xlst)
-        sda.sparse_decode_attn(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan, dec.meta,
-                               dec.num_splits, dec.workspace, out, lse)
+        if v41:  # Q RoPE, decode, combine with the inverse RoPE and MXFP8 cast
+            sda.sparse_decode_attn_v41(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
+                                       dec.meta, dec.num_splits, dec.workspace, dw.positions, dw.cos_sin, out8, osc,
+                                       lse)
+        else:
+            sda.sparse_decode_attn(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
+                                   dec.meta, dec.num_splits, dec.workspace, out, lse)
 
     log(f"[bench] plan {plan}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -220,10 +233,11 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] step {ms_step * 1e3:.2f} us")
 
-    # the decode kernel alone, back to back on the same stream
+    # the decode kernel alone, back to back on the same stream, launched as in the step (V4.1: every token
+    # leaves as a partial; the rotation of q changes values, not work)
     def decode_only():
         sda.decode_splits(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan, dec.meta,
-                          dec.num_splits, dec.workspace, out, lse)
+                          dec.num_splits, dec.workspace, None if v41 else out, None if v41 else lse)
 
     for _ in range(max(5, args.warmup // 2)):
         decode_only()
@@ -270,7 +284,7 @@ def main():
                    "list_width": w.lst.width, "extra_width": X,
                    "format": wl.FORMAT_NAMES[w.cache.fmt],
                    "extra_format": wl.FORMAT_NAMES[w.xcache.fmt] if w.xcache is not None else None,
-                   "sink": w.sink is not None, "valid_rows": rows,
+                   "sink": w.sink is not None, "valid_rows": rows, "v41_rope_mxfp8_out": v41,
                    "plan": {"num_parts": plan.num_parts, "heads_per_group": plan.heads_per_group,
                             "fixed_overhead": plan.fixed_overhead, "precision": plan.precision}},
         "tflops": round(flops / t_step / 1e12, 2),

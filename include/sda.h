@@ -192,7 +192,8 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
  * and checks as sda_sparse_decode_attn, but meta and num_splits are required and no combine runs.
  * Tokens touched by a single part get their final out/lse rows; the others get normalized fp32
  * partials in the workspace (o_accum at offset 0, lse_accum after it, as laid out by
- * sda_workspace_bytes) for a later sda_combine_splits. */
+ * sda_workspace_bytes) for a later sda_combine_splits. With out NULL (lse then unused) every token
+ * leaves as a partial, as in the V4.1 call. */
 int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
                       const sda_cache* cache /*host*/, const sda_list* list /*host*/,
                       const sda_cache* extra_cache /*host, nullable*/, const sda_list* extra_list /*host, nullable*/,
@@ -200,6 +201,49 @@ int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
                       const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
                       void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                       void* stream);
+
+/* The V4.1 decode call (vLLM swapab_decode_attn: Q RoPE in stage_inputs; inverse RoPE and the MXFP8
+ * output cast in device kernel step 9): q is taken before RoPE and the output leaves as fp8 with one
+ * ue8m0 scale per 32 dims. RoPE covers dims [448, 512) as 32 GPT-J pairs (dims 448 + 2i, 449 + 2i),
+ * rotated in fp32 (e' = fma(e, cos, -(o sin)), o' = fma(o, cos, e sin)) and rounded to bf16.
+ *  positions     int64 [T], device: each token's position.
+ *  cos_sin       fp32 [num_positions][cs_stride], device, 16-byte aligned: row p holds cos of pair i
+ *                at [i] and its sin at [32 + i]; cs_stride >= 64 and a multiple of 4. A position
+ *                outside [0, num_positions) rotates nothing (cos 1, sin 0).
+ *  out_fp8       e4m3fn codes [T][H][512], code (t, h, d) at out_fp8[t*of_stride_t + h*of_stride_h + d];
+ *                16-byte aligned, strides multiples of 16 bytes.
+ *  out_scale     ue8m0 bytes [T][H][16], byte (t, h, c) at out_scale[t*os_stride_t + h*os_stride_h + c]
+ *                for dims 32c .. 32c+31.
+ * Per token and head, with x = the attention output in fp32 and its dims 448..511 rotated back per pair
+ * (e' = fma(e, cos, sin o), o' = fma(o, cos, -(sin e))): per 32-dim chunk, amax = max(max |x|, 1e-10),
+ * scale byte = the ue8m0 of amax * (1/448) rounded up to a power of two, codes = e4m3(x * 2^(127 - byte))
+ * rounded to nearest even. */
+typedef struct sda_v41 {
+  const int64_t* positions;
+  const float* cos_sin;
+  int64_t cs_stride;
+  int64_t num_positions;
+  uint8_t* out_fp8;
+  int64_t of_stride_t, of_stride_h;
+  uint8_t* out_scale;
+  int64_t os_stride_t, os_stride_h;
+} sda_v41;
+
+/* Host only. Workspace of sda_sparse_decode_attn_v41: that of sda_workspace_bytes(T, H, 512, plan)
+ * plus the rotated q (bf16 [T][H][512]). */
+size_t sda_workspace_bytes_v41(int T, int H, const sda_plan* plan /*host*/);
+
+/* V4.1 decode: the arguments of sda_sparse_decode_attn with d_qk = d_v = 512, the bf16 output replaced
+ * by `v41` (host descriptor, device buffers) and lse optional (NULL: not written). Every token passes
+ * through the combine, where the output cast happens. Errors as sda_sparse_decode_attn, plus
+ * SDA_ERR_INVALID_ARG for a bad v41 descriptor. */
+int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
+                               const sda_cache* cache /*host*/, const sda_list* list /*host*/,
+                               const sda_cache* extra_cache /*host, nullable*/,
+                               const sda_list* extra_list /*host, nullable*/, const float* attn_sink, float scale,
+                               const sda_plan* plan /*host*/, const int32_t* meta, const int32_t* num_splits,
+                               void* workspace, size_t workspace_bytes, const sda_v41* v41 /*host*/,
+                               float* lse /*nullable*/, int64_t lse_stride_t, void* stream);
 
 /* Host only. Byte offsets of lse_accum in the workspace of this plan (o_accum starts at 0). */
 size_t sda_workspace_lse_offset(int T, int H, int d_v, const sda_plan* plan /*host*/);

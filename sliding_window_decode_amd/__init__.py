@@ -23,7 +23,7 @@ SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_HIP
 EXPORTED_SYMBOLS = ("sda_make_plan", "sda_workspace_bytes", "sda_get_sched_meta", "sda_get_sched_meta_host",
                     "sda_sparse_decode_attn", "sda_decode_splits", "sda_workspace_lse_offset",
                     "sda_combine_splits", "sda_status_string", "sda_last_error", "sda_record_bytes",
-                    "sda_format_dims")
+                    "sda_format_dims", "sda_workspace_bytes_v41", "sda_sparse_decode_attn_v41")
 
 
 class SdaError(RuntimeError):
@@ -40,6 +40,13 @@ class sda_cache(ctypes.Structure):
 class sda_list(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("row_stride", ctypes.c_int64), ("width", ctypes.c_int32),
                 ("queries_per_len", ctypes.c_int32), ("lens", ctypes.c_void_p)]
+
+
+class sda_v41(ctypes.Structure):
+    _fields_ = [("positions", ctypes.c_void_p), ("cos_sin", ctypes.c_void_p), ("cs_stride", ctypes.c_int64),
+                ("num_positions", ctypes.c_int64), ("out_fp8", ctypes.c_void_p), ("of_stride_t", ctypes.c_int64),
+                ("of_stride_h", ctypes.c_int64), ("out_scale", ctypes.c_void_p), ("os_stride_t", ctypes.c_int64),
+                ("os_stride_h", ctypes.c_int64)]
 
 
 class sda_plan(ctypes.Structure):
@@ -74,6 +81,13 @@ def lib():
                                              ctypes.POINTER(sda_list), vp, ctypes.c_float, ctypes.POINTER(sda_plan),
                                              vp, vp, vp, sz, vp, i64, i64, vp, i64, vp]
         L.sda_decode_splits.argtypes = L.sda_sparse_decode_attn.argtypes
+        L.sda_workspace_bytes_v41.argtypes = [i32, i32, ctypes.POINTER(sda_plan)]
+        L.sda_workspace_bytes_v41.restype = sz
+        L.sda_sparse_decode_attn_v41.argtypes = [vp, i64, i64, i32, i32, ctypes.POINTER(sda_cache),
+                                                 ctypes.POINTER(sda_list), ctypes.POINTER(sda_cache),
+                                                 ctypes.POINTER(sda_list), vp, ctypes.c_float,
+                                                 ctypes.POINTER(sda_plan), vp, vp, vp, sz, ctypes.POINTER(sda_v41),
+                                                 vp, i64, vp]
         L.sda_workspace_lse_offset.argtypes = [i32, i32, i32, ctypes.POINTER(sda_plan)]
         L.sda_workspace_lse_offset.restype = sz
         L.sda_combine_splits.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i64, i64, vp, i64, vp]
@@ -164,7 +178,7 @@ def get_sched_meta_host(T: int, lens, width: int, extra_lens, extra_width: int, 
 def _decode_call(fn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits, workspace,
                  out, lse, stream):
     T, H, d_qk = q.shape
-    d_v = out.shape[-1]
+    d_v = 512 if out is None else out.shape[-1]
     cc, cl = cache.c(), lst.c()
     xc = extra_cache.c() if extra_cache is not None else None
     xl = extra_lst.c() if extra_lst is not None else None
@@ -173,7 +187,8 @@ def _decode_call(fn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, pl
         ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
         _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)))
+        _ptr(out), 0 if out is None else out.stride(0), 0 if out is None else out.stride(1), _ptr(lse),
+        0 if lse is None else lse.stride(0), _stream(stream)))
 
 
 def sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
@@ -186,9 +201,33 @@ def sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cac
 
 def decode_splits(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
                   attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, out, lse, stream=None):
-    """The decode kernel only (final rows for unsplit tokens, partials in the workspace for the others)."""
+    """The decode kernel only (final rows for unsplit tokens, partials in the workspace for the others; with
+    out=None every token leaves as a partial, as in the V4.1 call)."""
     _decode_call(lib().sda_decode_splits, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta,
                  num_splits, workspace, out, lse, stream)
+
+
+def workspace_bytes_v41(T: int, H: int, plan: sda_plan) -> int:
+    return int(lib().sda_workspace_bytes_v41(T, H, ctypes.byref(plan)))
+
+
+def sparse_decode_attn_v41(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
+                           attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, positions, cos_sin,
+                           out_fp8, out_scale, lse=None, stream=None):
+    """V4.1 decode: q [T, H, 512] bf16 before RoPE, positions [T] int64, cos_sin [P, >=64] fp32; writes out_fp8
+    [T, H, 512] uint8 (e4m3 codes), out_scale [T, H, 16] uint8 (ue8m0) and, if given, lse [T, H] fp32."""
+    T, H, _ = q.shape
+    cc, cl = cache.c(), lst.c()
+    xc = extra_cache.c() if extra_cache is not None else None
+    xl = extra_lst.c() if extra_lst is not None else None
+    v = sda_v41(_ptr(positions), _ptr(cos_sin), cos_sin.stride(0), cos_sin.shape[0], _ptr(out_fp8), out_fp8.stride(0),
+                out_fp8.stride(1), _ptr(out_scale), out_scale.stride(0), out_scale.stride(1))
+    _check(lib().sda_sparse_decode_attn_v41(
+        _ptr(q), q.stride(0), q.stride(1), T, H, ctypes.byref(cc), ctypes.byref(cl),
+        ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
+        _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), ctypes.byref(v),
+        _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream)))
 
 
 def workspace_lse_offset(T: int, H: int, d_v: int, plan: sda_plan) -> int:
@@ -215,6 +254,8 @@ class Decoder:
         self.meta = torch.empty((self.plan.num_parts, META_INTS), dtype=torch.int32, device=device)
         self.num_splits = torch.empty(T + 1, dtype=torch.int32, device=device)
         nbytes = workspace_bytes(T, H, 512, self.plan)
+        if d_qk == 512:  # room for the V4.1 call's rotated q as well
+            nbytes = max(nbytes, workspace_bytes_v41(T, H, self.plan))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def schedule(self, lst: SlotList, extra: Optional[SlotList] = None, stream=None):
@@ -234,3 +275,19 @@ class Decoder:
         sparse_decode_attn(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, self.meta,
                            self.num_splits, self.workspace, out, lse, stream)
         return out, lse
+
+    def v41(self, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, positions, cos_sin, out_fp8=None,
+            out_scale=None, lse=None, schedule=True, stream=None):
+        """The V4.1 call (Q RoPE, decode, inverse RoPE and MXFP8 output): returns (out_fp8, out_scale, lse)."""
+        import torch
+        if out_fp8 is None:
+            out_fp8 = torch.empty((self.T, self.H, 512), dtype=torch.uint8, device=q.device)
+        if out_scale is None:
+            out_scale = torch.empty((self.T, self.H, 16), dtype=torch.uint8, device=q.device)
+        if lse is None:
+            lse = torch.empty((self.T, self.H), dtype=torch.float32, device=q.device)
+        if schedule:
+            self.schedule(lst, extra_lst, stream)
+        sparse_decode_attn_v41(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, self.meta,
+                               self.num_splits, self.workspace, positions, cos_sin, out_fp8, out_scale, lse, stream)
+        return out_fp8, out_scale, lse

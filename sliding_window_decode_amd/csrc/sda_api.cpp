@@ -102,6 +102,7 @@ int check_plan(const sda_plan* plan, int H) {
 
 struct WorkspaceLayout {
   size_t o_acc, lse_acc, meta, num_splits, total;
+  size_t q_rot, total_v41;  // V4.1 calls: the rotated q after everything else
 };
 
 WorkspaceLayout layout_of(int T, int H, int d_v, int P) {
@@ -112,6 +113,8 @@ WorkspaceLayout layout_of(int T, int H, int d_v, int P) {
   w.meta = round_up(w.lse_acc + splits * H * sizeof(float), 256);
   w.num_splits = round_up(w.meta + (size_t)P * SDA_META_INTS * sizeof(int32_t), 256);
   w.total = round_up(w.num_splits + ((size_t)T + 1) * sizeof(int32_t), 256);
+  w.q_rot = w.total;
+  w.total_v41 = round_up(w.q_rot + (size_t)T * H * 512 * sizeof(uint16_t), 256);
   return w;
 }
 
@@ -320,17 +323,20 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
                       const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
                       const sda_list* extra_list, const sda_plan* plan, const int32_t* meta, const int32_t* num_splits,
                       void* workspace, size_t workspace_bytes, void* out, int64_t out_stride_t, int64_t out_stride_h,
-                      float* lse, int64_t lse_stride_t) {
-  if (!q || !out || !lse) return fail(SDA_ERR_INVALID_ARG, "q, out and lse are required");
+                      float* lse, int64_t lse_stride_t, bool no_out = false, bool v41 = false) {
+  // no_out: no bf16 output and an optional lse (V4.1 calls, whose fp8 output is checked by the caller, and
+  // decode-only calls that leave every token as a partial)
+  if (!q) return fail(SDA_ERR_INVALID_ARG, "q is required");
+  if (!no_out && (!out || !lse)) return fail(SDA_ERR_INVALID_ARG, "q, out and lse are required");
   if (T < 1) return fail(SDA_ERR_INVALID_ARG, "T must be >= 1");
   if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
   if (!((d_qk == 512 || d_qk == 576) && d_v == 512))
     return fail(SDA_ERR_UNSUPPORTED, "(d_qk, d_v) must be (512, 512) or (576, 512)");
   if (!aligned(q, 16) || q_stride_h % 8 || q_stride_t % 8 || q_stride_h < d_qk || q_stride_t < 0)
     return fail(SDA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
-  if (!aligned(out, 16) || out_stride_h % 8 || out_stride_t % 8 || out_stride_h < d_v || out_stride_t < 0)
+  if (!no_out && (!aligned(out, 16) || out_stride_h % 8 || out_stride_t % 8 || out_stride_h < d_v || out_stride_t < 0))
     return fail(SDA_ERR_INVALID_ARG, "out must be 16-byte aligned with strides that are multiples of 8 elements");
-  if (lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
+  if (lse && lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
   int rc;
   if ((rc = check_cache(cache, d_qk, "main"))) return rc;
   if ((rc = check_list(list, "main"))) return rc;
@@ -345,7 +351,26 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
     return fail(SDA_ERR_INVALID_ARG, "meta and num_splits must be given together");
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
   if (!workspace || !aligned(workspace, 256)) return fail(SDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < wl.total) return fail(SDA_ERR_WORKSPACE, "workspace smaller than sda_workspace_bytes()");
+  if (workspace_bytes < (v41 ? wl.total_v41 : wl.total))
+    return fail(SDA_ERR_WORKSPACE, v41 ? "workspace smaller than sda_workspace_bytes_v41()"
+                                       : "workspace smaller than sda_workspace_bytes()");
+  return SDA_OK;
+}
+
+int check_v41(const sda_v41* v, int T, int H) {
+  if (!v) return fail(SDA_ERR_INVALID_ARG, "v41 descriptor is NULL");
+  if (!v->positions || !v->cos_sin || !v->out_fp8 || !v->out_scale)
+    return fail(SDA_ERR_INVALID_ARG, "v41: positions, cos_sin, out_fp8 and out_scale are required");
+  if (!aligned(v->positions, 8) || !aligned(v->cos_sin, 16) || v->cs_stride < 64 || v->cs_stride % 4 ||
+      v->num_positions < 0)
+    return fail(SDA_ERR_INVALID_ARG, "v41: cos_sin must be 16-byte aligned with a stride >= 64 and a multiple of 4");
+  if (!aligned(v->out_fp8, 16) || v->of_stride_h < 512 || v->of_stride_h % 16 || v->of_stride_t < 0 ||
+      v->of_stride_t % 16)
+    return fail(SDA_ERR_INVALID_ARG, "v41: out_fp8 must be 16-byte aligned with strides in 16s, of_stride_h >= 512");
+  if (v->os_stride_h < 16 || v->os_stride_t < 0)
+    return fail(SDA_ERR_INVALID_ARG, "v41: os_stride_h must be >= 16");
+  (void)T;
+  (void)H;
   return SDA_OK;
 }
 
@@ -413,15 +438,18 @@ int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
                       const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
                       void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                       void* stream) {
+  // out NULL: every token leaves as a partial in the workspace (lse is then not used)
+  const bool no_out = out == nullptr;
   int rc = check_decode_args(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, plan,
                              meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h, lse,
-                             lse_stride_t);
+                             lse_stride_t, no_out);
   if (rc) return rc;
   if (!meta) return fail(SDA_ERR_INVALID_ARG, "sda_decode_splits needs meta and num_splits");
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
-  const sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
-                                            attn_sink, scale, meta, num_splits, (char*)workspace, wl, out,
-                                            out_stride_t, out_stride_h, lse, lse_stride_t);
+  sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
+                                      attn_sink, scale, meta, num_splits, (char*)workspace, wl, out, out_stride_t,
+                                      out_stride_h, no_out ? nullptr : lse, lse_stride_t);
+  p.all_partial = no_out ? 1 : 0;
   hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
@@ -473,6 +501,72 @@ int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float*
   const sda::CombineParams c = combine_params(T, H, o_accum, lse_accum, num_splits, attn_sink, out, out_stride_t,
                                              out_stride_h, lse, lse_stride_t);
   hipError_t e = sda::launch_combine(c, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return SDA_OK;
+}
+
+
+size_t sda_workspace_bytes_v41(int T, int H, const sda_plan* plan) {
+  if (!plan || T < 1 || H < 1 || plan->num_parts < 1) return 0;
+  return layout_of(T, H, 512, plan->num_parts).total_v41;
+}
+
+int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
+                               const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                               const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                               const int32_t* meta, const int32_t* num_splits, void* workspace,
+                               size_t workspace_bytes, const sda_v41* v41, float* lse, int64_t lse_stride_t,
+                               void* stream) {
+  int rc = check_decode_args(q, q_stride_t, q_stride_h, T, H, 512, 512, cache, list, extra_cache, extra_list, plan,
+                             meta, num_splits, workspace, workspace_bytes, nullptr, 0, 0, lse, lse_stride_t, true, true);
+  if (rc) return rc;
+  if ((rc = check_v41(v41, T, H))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const WorkspaceLayout wl = layout_of(T, H, 512, plan->num_parts);
+  if (!meta) {
+    int32_t* m = (int32_t*)(ws + wl.meta);
+    int32_t* ns = (int32_t*)(ws + wl.num_splits);
+    hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
+    if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
+    meta = m;
+    num_splits = ns;
+  }
+  // prologue: q with its RoPE dims rotated, into the workspace
+  sda::RopeParams rp;
+  memset(&rp, 0, sizeof(rp));
+  rp.q = (const uint16_t*)q;
+  rp.q_st = q_stride_t;
+  rp.q_sh = q_stride_h;
+  rp.q_out = (uint16_t*)(ws + wl.q_rot);
+  rp.positions = v41->positions;
+  rp.cos_sin = v41->cos_sin;
+  rp.cs_stride = v41->cs_stride;
+  rp.num_positions = v41->num_positions;
+  rp.T = T;
+  rp.H = H;
+  hipError_t e = sda::launch_rope_q(rp, st);
+  if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
+  // decode on the rotated q, every token leaving as an fp32 partial
+  sda::DecodeParams p = decode_params(rp.q_out, (int64_t)H * 512, 512, T, H, cache, list, extra_cache, extra_list,
+                                      attn_sink, scale, meta, num_splits, ws, wl, nullptr, 0, 0, nullptr, 0);
+  p.all_partial = 1;
+  e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, 512, plan->precision, st);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  // combine every token: merge, inverse RoPE, MXFP8
+  sda::CombineParams c = combine_params(T, H, p.o_acc, p.lse_acc, num_splits, attn_sink, nullptr, 0, 0, lse,
+                                        lse_stride_t);
+  c.positions = v41->positions;
+  c.cos_sin = v41->cos_sin;
+  c.cs_stride = v41->cs_stride;
+  c.num_positions = v41->num_positions;
+  c.o8 = v41->out_fp8;
+  c.o8_st = v41->of_stride_t;
+  c.o8_sh = v41->of_stride_h;
+  c.osc = v41->out_scale;
+  c.osc_st = v41->os_stride_t;
+  c.osc_sh = v41->os_stride_h;
+  e = sda::launch_combine(c, st);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return SDA_OK;
 }

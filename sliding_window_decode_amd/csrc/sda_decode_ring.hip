@@ -561,7 +561,7 @@ void decode_ring_kernel(DecodeParams p) {
     if (it1.end() || it1.t != it0.t) {
       ep_t = it0.t;
       ep_s = it0.s_first;
-      ep_n = it0.whole;
+      ep_n = it0.whole && !p.all_partial;
     }
     if (it1.end()) break;
 #pragma unroll

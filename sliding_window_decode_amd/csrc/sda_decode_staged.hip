@@ -392,7 +392,7 @@ void decode_kernel(DecodeParams p) {
     if (it1.end() || it1.t != it0.t) {
       const int t = it0.t;
       const int s_first = it0.s_first;
-      const bool whole = it0.whole;
+      const bool whole = it0.whole && !p.all_partial;
       const int split_k = (t == bt) ? bk : 0;
 #pragma unroll
       for (int hb = 0; hb < NH2; ++hb) {

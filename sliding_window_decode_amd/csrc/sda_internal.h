@@ -44,6 +44,18 @@ struct DecodeParams {
   int nlists;
   int T, H;
   float scale_log2;          // softmax scale * log2(e)
+  int all_partial;           // every token leaves as an fp32 partial (the combine finishes them all)
+};
+
+// The V4.1 call's RoPE inputs (cos_sin row p: cos of pair i at [i], sin at [32 + i]).
+struct RopeParams {
+  const uint16_t* q;         // bf16 bits, [T][H][512] with strides
+  int64_t q_st, q_sh;
+  uint16_t* q_out;           // [T][H][512] contiguous
+  const int64_t* positions;  // [T]
+  const float* cos_sin;
+  int64_t cs_stride, num_positions;
+  int T, H;
 };
 
 struct SchedParams {
@@ -65,9 +77,18 @@ struct CombineParams {
   const float* sink;
   uint16_t* out;
   int64_t o_st, o_sh;
-  float* lse;
+  float* lse;                // nullptr: not written (V4.1 calls only)
   int64_t l_st;
   int T, H;
+  // V4.1 output (o8 != nullptr): every token is merged here, its dims 448..511 rotated back and the
+  // result cast to MXFP8 (e4m3 codes + one ue8m0 byte per 32 dims) instead of bf16
+  const int64_t* positions;
+  const float* cos_sin;
+  int64_t cs_stride, num_positions;
+  uint8_t* o8;
+  int64_t o8_st, o8_sh;
+  uint8_t* osc;
+  int64_t osc_st, osc_sh;
 };
 
 // ---------------------------------------------------------------- scheduling math (host + device)
@@ -108,5 +129,6 @@ hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_rope_q(const RopeParams& p, hipStream_t stream);
 
 }  // namespace sda

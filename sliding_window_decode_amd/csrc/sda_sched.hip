@@ -4,7 +4,9 @@
 // max(1, ceil(n_main/64) + ceil(n_extra/64)) tiles plus a fixed overhead F; the concatenated
 // (token, tile) sequence is cut into num_parts contiguous parts of equal cost (see sda_internal.h).
 // Combine (FlashMLA run_flash_mla_combine_kernel; vLLM swapab_decode_attn step 9): LSE-weighted sum
-// of the normalized partials of every split token, the sink folded into the denominator once.
+// of the normalized partials of every split token, the sink folded into the denominator once. In a
+// V4.1 call every token comes through here and leaves as MXFP8 (vLLM swapab_decode_attn step 9: the
+// inverse RoPE of dims 448..511 and the cast with one ue8m0 scale per 32 dims).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -106,6 +108,58 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
   }
 }
 
+// V4.1 output of one (token, head, 32-dim chunk): x = merged output (0 when the token has no rows or an
+// infinite sink), dims 448..511 rotated back per GPT-J pair in fp32, then amax = max(max |x|, 1e-10),
+// scale byte = ue8m0 of amax * (1/448) rounded up to a power of two, codes = e4m3(x * 2^(127 - byte))
+// (v_cvt_pk_fp8_f32: round to nearest even; |x * 2^(127 - byte)| stays within 448 up to one rounding
+// of the product, which still rounds to 448).
+__device__ __forceinline__ void mxfp8_store(const CombineParams& p, int t, int h, int d0, bool ok, float den,
+                                            const f32x4 (&acc)[8]) {
+  float x[32];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[4 * e + k] = ok ? acc[e][k] / den : 0.f;
+  }
+  if (d0 >= 448) {
+    const int64_t pos = p.positions[t];
+    if (pos >= 0 && pos < p.num_positions) {
+      const float* cs = p.cos_sin + pos * p.cs_stride + (d0 - 448) / 2;  // pairs (d0 - 448) / 2 .. + 15
+      f32x4 cv[4], sv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cv[j] = *(const f32x4*)(cs + 4 * j);
+        sv[j] = *(const f32x4*)(cs + 32 + 4 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float c = cv[j >> 2][j & 3], s = sv[j >> 2][j & 3];
+        const float oe = x[2 * j], oo = x[2 * j + 1];
+        x[2 * j] = __builtin_fmaf(oe, c, s * oo);
+        x[2 * j + 1] = __builtin_fmaf(oo, c, -(s * oe));
+      }
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  amax = fmaxf(amax, 1e-10f);
+  const uint32_t yb = __builtin_bit_cast(uint32_t, amax * (float)(1.0 / 448.0));
+  const uint32_t ex = ((yb >> 23) & 0xFFu) + ((yb & 0x7FFFFFu) != 0u ? 1u : 0u);
+  const float inv = __builtin_bit_cast(float, (254u - ex) << 23);
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, v, true);
+    w[q] = (uint32_t)v;
+  }
+  uint8_t* o = p.o8 + (int64_t)t * p.o8_st + (int64_t)h * p.o8_sh + d0;
+  *(u32x4*)o = u32x4{w[0], w[1], w[2], w[3]};
+  *(u32x4*)(o + 16) = u32x4{w[4], w[5], w[6], w[7]};
+  p.osc[(int64_t)t * p.osc_st + (int64_t)h * p.osc_sh + (d0 >> 5)] = (uint8_t)ex;
+}
+
 // One workgroup per (token, block of 16 heads); thread (head h = tid / 16, 32 dims from 32 * (tid % 16)).
 // The splits are read four at a time with every load of a batch issued before any is used (a token
 // rarely has more than a few splits), so a merge costs about one global round trip per batch.
@@ -113,7 +167,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int t = blockIdx.x;
   const int s0 = p.num_splits[t];
   const int n = p.num_splits[t + 1] - s0;
-  if (n < 2) return;
+  const bool v41 = p.o8 != nullptr;
+  if (n < (v41 ? 1 : 2)) return;
   const int tid = threadIdx.x;
   const int h = blockIdx.y * 16 + (tid >> 4);
   const int d0 = 32 * (tid & 15);
@@ -158,6 +213,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
       for (int e = 0; e < 8; ++e) acc[e] += wj * v[j][e];
     }
     M = bm;
+  }
+  if (v41) {
+    const bool ok = !(M == kNegInf || M == kPosInf);
+    mxfp8_store(p, t, h, d0, ok, den, acc);
+    if (p.lse && (tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = ok ? M + logf(den) : M;
+    return;
   }
   if (M == kNegInf || M == kPosInf) {
     for (int e = 0; e < 32; e += 8) *(u32x4*)(orow + e) = u32x4{0u, 0u, 0u, 0u};

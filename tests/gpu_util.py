@@ -38,6 +38,9 @@ class DeviceWorkload:
         self.xcache = dev_cache(w.xcache, device) if w.xcache is not None else None
         self.xlst = dev_list(w.xlst, device) if w.xlst is not None else None
         self.sink = torch.from_numpy(w.sink).to(device) if w.sink is not None else None
+        rope = getattr(w, "rope", None)
+        self.positions = torch.from_numpy(rope.positions).to(device) if rope is not None else None
+        self.cos_sin = torch.from_numpy(rope.cos_sin).to(device) if rope is not None else None
 
     def run(self, plan=None, sink="default", q=None, out=None, lse=None):
         w = self.w
@@ -48,6 +51,60 @@ class DeviceWorkload:
                    out=out, lse=lse)
         torch.cuda.synchronize()
         return o, l, dec
+
+
+    def run_v41(self, plan=None):
+        """The V4.1 call: returns (codes, scale bytes, lse, decoder)."""
+        w = self.w
+        dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0,
+                          device=self.q.device, plan=plan)
+        c, s, l = dec.v41(self.q, self.cache, self.lst, self.xcache, self.xlst, self.sink, w.scale, self.positions,
+                          self.cos_sin)
+        torch.cuda.synchronize()
+        return c, s, l, dec
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def compare_v41(codes_gpu, scales_gpu, lse_gpu, codes_ref, scales_ref, l_ref, what="", exact=False):
+    """MXFP8 output against the oracle's cast of its own result. The cast is decided in fp32 on both sides
+    from values that differ by the attention's rounding (about 1e-6 relative), so an element may land one e4m3
+    step away where its value sits that close to a rounding midpoint, and a chunk's scale byte one away where
+    its amax / 448 sits that close to a power of two. Bar: decoded values (code x 2^(byte - 127)) within one
+    e4m3 step (at the coarser of the two scales) of the oracle's; elements that differ at all at most 1 in
+    10^3 (and at most 2 in smaller outputs); LSE within 1e-3. exact=True: codes and scales bit-identical."""
+    cg = codes_gpu.cpu().numpy() if hasattr(codes_gpu, "cpu") else codes_gpu
+    sg = scales_gpu.cpu().numpy() if hasattr(scales_gpu, "cpu") else scales_gpu
+    lg = lse_gpu.float().cpu().numpy().astype(np.float64)
+    if exact:
+        assert np.array_equal(sg, scales_ref), f"{what}: scale bytes differ"
+        assert np.array_equal(cg, codes_ref), f"{what}: codes differ"
+    assert np.all((cg & 0x7F) != 0x7F), f"{what}: NaN codes"
+    sdiff = np.abs(sg.astype(np.int32) - scales_ref.astype(np.int32))
+    assert sdiff.max() <= 1, f"{what}: scale bytes differ by {sdiff.max()}"
+    sgx = np.repeat(sg.astype(np.float64), 32, axis=-1) - 127
+    srx = np.repeat(scales_ref.astype(np.float64), 32, axis=-1) - 127
+    dg = e4m3_decode(cg) * np.exp2(sgx)
+    dr = e4m3_decode(codes_ref) * np.exp2(srx)
+    coarse = np.maximum(sgx, srx)
+    mag = np.maximum(np.abs(dg), np.abs(dr)) / np.exp2(coarse)        # in units of the coarser scale
+    step = np.where(mag < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(mag, 1e-300))) - 3))
+    err = np.abs(dg - dr) / np.exp2(coarse)
+    n_diff = int((cg != codes_ref).sum())
+    info = dict(scale_diffs=int((sdiff > 0).sum()), code_diffs=n_diff, n=int(cg.size),
+                max_err_steps=float((err / step).max()) if err.size else 0.0)
+    assert np.all(err <= step * (1 + 1e-9)), f"{what}: decoded values beyond one e4m3 step {info}"
+    assert n_diff <= max(2, cg.size // 1000), f"{what}: too many differing codes {info}"
+    inf_ref = ~np.isfinite(l_ref)
+    assert np.array_equal(inf_ref, ~np.isfinite(lg)), f"{what}: LSE infinities differ"
+    if (~inf_ref).any():
+        lse_err = float(np.abs(lg[~inf_ref] - l_ref[~inf_ref]).max())
+        info["lse_max_abs"] = lse_err
+        assert lse_err <= LSE_MAX_ABS, f"{what}: lse max-abs {lse_err:.3e} {info}"
+    return info
 
 
 def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", count_flips=True):

@@ -264,3 +264,51 @@ def test_host_scheduler_rejects_negative_queries_per_len():
     with pytest.raises(sda.SdaError) as ei:
         sda.get_sched_meta_host(4, None, 128, None, 0, plan, queries_per_len=-1)
     assert ei.value.status == sda.SDA_ERR_INVALID_ARG
+
+
+class _V41Bufs:
+    def __init__(self, T=4, H=16, cs_ptr=1 << 34, cs_stride=64, of_stride_h=512, os_stride_h=16, of_ptr=1 << 35):
+        self.positions = _FakeTensor((T,), 1 << 36, itemsize=8)
+        self.cos_sin = _FakeTensor((100, cs_stride), cs_ptr, strides=(cs_stride, 1), itemsize=4)
+        self.out_fp8 = _FakeTensor((T, H, 512), of_ptr, strides=(H * of_stride_h, of_stride_h, 1), itemsize=1)
+        self.out_scale = _FakeTensor((T, H, 16), 1 << 37, strides=(H * os_stride_h, os_stride_h, 1), itemsize=1)
+
+
+def _call_v41(q_shape=(4, 16, 512), fmt=sda.FP8_UE8M0, ws_bytes=None, **kw):
+    T, H, dqk = q_shape
+    rec = {1: 528, 3: 656, 4: 528, 5: 584}[fmt]
+    q = _FakeTensor(q_shape)
+    cache = sda.Cache(_FakeTensor((1,), 1 << 24), 16, 64, 64 * rec, fmt, None)
+    lst = sda.SlotList(_FakeTensor((T, 128), 1 << 27), 128, None)
+    plan = sda.sda_plan(8, 16, 2, 2)
+    need = sda.workspace_bytes_v41(T, H, plan)
+    ws = _FakeTensor((need if ws_bytes is None else ws_bytes,), 1 << 30, itemsize=1)
+    b = _V41Bufs(T, H, **kw)
+    sda.sparse_decode_attn_v41(q, cache, lst, None, None, None, 0.05, plan, None, None, ws, b.positions, b.cos_sin,
+                               b.out_fp8, b.out_scale, None, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=sda.V32_656, q_shape=(4, 16, 576)), sda.SDA_ERR_UNSUPPORTED),  # V4.1 rows hold 512 dims
+    (dict(cs_ptr=(1 << 34) + 4), sda.SDA_ERR_INVALID_ARG),                     # cos_sin misaligned
+    (dict(cs_stride=48), sda.SDA_ERR_INVALID_ARG),                             # cos_sin row too short
+    (dict(cs_stride=66), sda.SDA_ERR_INVALID_ARG),                             # stride not a multiple of 4
+    (dict(of_stride_h=520), sda.SDA_ERR_INVALID_ARG),                          # out_fp8 stride not in 16s
+    (dict(of_ptr=(1 << 35) + 8), sda.SDA_ERR_INVALID_ARG),                     # out_fp8 misaligned
+    (dict(os_stride_h=8), sda.SDA_ERR_INVALID_ARG),                            # scale row too short
+    (dict(ws_bytes=1024), sda.SDA_ERR_WORKSPACE),                              # workspace too small
+])
+def test_v41_rejects_bad_arguments_on_the_host(kw, status):
+    with pytest.raises(sda.SdaError) as ei:
+        _call_v41(**kw)
+    assert ei.value.status == status
+
+
+def test_v41_workspace_holds_the_rotated_q():
+    plan = sda.sda_plan(64, 32, 2, 2)
+    for T, H in ((1, 16), (256, 32), (64, 128)):
+        assert sda.workspace_bytes_v41(T, H, plan) >= sda.workspace_bytes(T, H, 512, plan) + T * H * 1024
+    # the standard workspace is not enough for a V4.1 call
+    with pytest.raises(sda.SdaError) as ei:
+        _call_v41(ws_bytes=sda.workspace_bytes(4, 16, 512, sda.sda_plan(8, 16, 2, 2)))
+    assert ei.value.status == sda.SDA_ERR_WORKSPACE

@@ -26,7 +26,7 @@ def _log(msg):
 
 
 SMALL_T = {"c1_tiny_swa": 4, "c2_swa_h128": 6, "c3_swa_fp8extra": 12, "c4_swa_nvfp4extra": 6, "c5_topk_v32": 3,
-           "c6_swa_ue8m0": 12, "c7_swa_model1": 12}
+           "c6_swa_ue8m0": 12, "c7_swa_model1": 12, "c8_v41_ue8m0": 12}
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
