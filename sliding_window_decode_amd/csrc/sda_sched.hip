@@ -113,31 +113,43 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
 // scale byte = ue8m0 of amax * (1/448) rounded up to a power of two, codes = e4m3(x * 2^(127 - byte))
 // (v_cvt_pk_fp8_f32: round to nearest even; |x * 2^(127 - byte)| stays within 448 up to one rounding
 // of the product, which still rounds to 448).
+// The cos / sin of the 16 pairs of a thread's chunk (dims >= 448; identity for a position outside the
+// table), loaded before the merge so that their latency overlaps that of the partials.
+struct ChunkRope {
+  f32x4 cv[4], sv[4];
+  bool on;
+  __device__ __forceinline__ void load(const CombineParams& p, int t, int d0) {
+    on = false;
+    if (d0 >= 448) {
+      const int64_t pos = p.positions[t];
+      if (pos >= 0 && pos < p.num_positions) {
+        const float* cs = p.cos_sin + pos * p.cs_stride + (d0 - 448) / 2;  // pairs (d0 - 448) / 2 .. + 15
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cv[j] = *(const f32x4*)(cs + 4 * j);
+          sv[j] = *(const f32x4*)(cs + 32 + 4 * j);
+        }
+        on = true;
+      }
+    }
+  }
+};
+
 __device__ __forceinline__ void mxfp8_store(const CombineParams& p, int t, int h, int d0, bool ok, float den,
-                                            const f32x4 (&acc)[8]) {
+                                            const f32x4 (&acc)[8], const ChunkRope& rope) {
   float x[32];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[4 * e + k] = ok ? acc[e][k] / den : 0.f;
   }
-  if (d0 >= 448) {
-    const int64_t pos = p.positions[t];
-    if (pos >= 0 && pos < p.num_positions) {
-      const float* cs = p.cos_sin + pos * p.cs_stride + (d0 - 448) / 2;  // pairs (d0 - 448) / 2 .. + 15
-      f32x4 cv[4], sv[4];
+  if (rope.on) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        cv[j] = *(const f32x4*)(cs + 4 * j);
-        sv[j] = *(const f32x4*)(cs + 32 + 4 * j);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float c = cv[j >> 2][j & 3], s = sv[j >> 2][j & 3];
-        const float oe = x[2 * j], oo = x[2 * j + 1];
-        x[2 * j] = __builtin_fmaf(oe, c, s * oo);
-        x[2 * j + 1] = __builtin_fmaf(oo, c, -(s * oe));
-      }
+    for (int j = 0; j < 16; ++j) {
+      const float c = rope.cv[j >> 2][j & 3], s = rope.sv[j >> 2][j & 3];
+      const float oe = x[2 * j], oo = x[2 * j + 1];
+      x[2 * j] = __builtin_fmaf(oe, c, s * oo);
+      x[2 * j + 1] = __builtin_fmaf(oo, c, -(s * oe));
     }
   }
   float amax = 0.f;
@@ -162,12 +174,15 @@ __device__ __forceinline__ void mxfp8_store(const CombineParams& p, int t, int h
 
 // One workgroup per (token, block of 16 heads); thread (head h = tid / 16, 32 dims from 32 * (tid % 16)).
 // The splits are read four at a time with every load of a batch issued before any is used (a token
-// rarely has more than a few splits), so a merge costs about one global round trip per batch.
+// rarely has more than a few splits), so a merge costs about one global round trip per batch. The V4.1
+// instance (every token, most with one or two splits) reads two at a time: its cast needs registers of
+// its own, and four waves per SIMD hide the round trips better than longer batches.
+template <bool V41>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr bool v41 = V41;
   const int t = blockIdx.x;
   const int s0 = p.num_splits[t];
   const int n = p.num_splits[t + 1] - s0;
-  const bool v41 = p.o8 != nullptr;
   if (n < (v41 ? 1 : 2)) return;
   const int tid = threadIdx.x;
   const int h = blockIdx.y * 16 + (tid >> 4);
@@ -175,7 +190,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const bool has_sink = p.sink != nullptr;
   const float sk = has_sink ? p.sink[h] : kNegInf;
   uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + d0;
-  constexpr int KB = 4;  // splits per batch
+  ChunkRope rope;
+  if constexpr (v41) rope.load(p, t, d0);
+  constexpr int KB = v41 ? 2 : 4;  // splits per batch
   // running merge state: max M, denominator den and accumulator relative to M
   float M = sk;
   float den = has_sink ? 1.0f : 0.0f;  // exp(sk - M) with M = sk
@@ -214,9 +231,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     M = bm;
   }
-  if (v41) {
+  if constexpr (v41) {
     const bool ok = !(M == kNegInf || M == kPosInf);
-    mxfp8_store(p, t, h, d0, ok, den, acc);
+    mxfp8_store(p, t, h, d0, ok, den, acc, rope);
     if (p.lse && (tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = ok ? M + logf(den) : M;
     return;
   }
@@ -247,7 +264,10 @@ hipError_t launch_sched(const SchedParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
+  if (p.o8)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
