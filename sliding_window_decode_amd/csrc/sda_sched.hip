@@ -108,107 +108,59 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
   }
 }
 
-// V4.1 output of one (token, head, 32-dim chunk): x = merged output (0 when the token has no rows or an
-// infinite sink), dims 448..511 rotated back per GPT-J pair in fp32, then amax = max(max |x|, 1e-10),
-// scale byte = ue8m0 of amax * (1/448) rounded up to a power of two, codes = e4m3(x * 2^(127 - byte))
-// (v_cvt_pk_fp8_f32: round to nearest even; |x * 2^(127 - byte)| stays within 448 up to one rounding
-// of the product, which still rounds to 448).
-// The cos / sin of the 16 pairs of a thread's chunk (dims >= 448; identity for a position outside the
-// table), loaded before the merge so that their latency overlaps that of the partials.
-struct ChunkRope {
-  f32x4 cv[4], sv[4];
-  bool on;
-  __device__ __forceinline__ void load(const CombineParams& p, int t, int d0) {
-    on = false;
-    if (d0 >= 448) {
-      const int64_t pos = p.positions[t];
-      if (pos >= 0 && pos < p.num_positions) {
-        const float* cs = p.cos_sin + pos * p.cs_stride + (d0 - 448) / 2;  // pairs (d0 - 448) / 2 .. + 15
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          cv[j] = *(const f32x4*)(cs + 4 * j);
-          sv[j] = *(const f32x4*)(cs + 32 + 4 * j);
-        }
-        on = true;
-      }
-    }
-  }
-};
-
-__device__ __forceinline__ void mxfp8_store(const CombineParams& p, int t, int h, int d0, bool ok, float den,
-                                            const f32x4 (&acc)[8], const ChunkRope& rope) {
-  float x[32];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) x[4 * e + k] = ok ? acc[e][k] / den : 0.f;
-  }
-  if (rope.on) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float c = rope.cv[j >> 2][j & 3], s = rope.sv[j >> 2][j & 3];
-      const float oe = x[2 * j], oo = x[2 * j + 1];
-      x[2 * j] = __builtin_fmaf(oe, c, s * oo);
-      x[2 * j + 1] = __builtin_fmaf(oo, c, -(s * oe));
-    }
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
-  amax = fmaxf(amax, 1e-10f);
-  const uint32_t yb = __builtin_bit_cast(uint32_t, amax * (float)(1.0 / 448.0));
-  const uint32_t ex = ((yb >> 23) & 0xFFu) + ((yb & 0x7FFFFFu) != 0u ? 1u : 0u);
-  const float inv = __builtin_bit_cast(float, (254u - ex) << 23);
-  uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, v, true);
-    w[q] = (uint32_t)v;
-  }
-  uint8_t* o = p.o8 + (int64_t)t * p.o8_st + (int64_t)h * p.o8_sh + d0;
-  *(u32x4*)o = u32x4{w[0], w[1], w[2], w[3]};
-  *(u32x4*)(o + 16) = u32x4{w[4], w[5], w[6], w[7]};
-  p.osc[(int64_t)t * p.osc_st + (int64_t)h * p.osc_sh + (d0 >> 5)] = (uint8_t)ex;
-}
-
-// One workgroup per (token, block of 16 heads); thread (head h = tid / 16, 32 dims from 32 * (tid % 16)).
-// The splits are read four at a time with every load of a batch issued before any is used (a token
-// rarely has more than a few splits), so a merge costs about one global round trip per batch. The V4.1
-// instance (every token, most with one or two splits) reads two at a time: its cast needs registers of
-// its own, and four waves per SIMD hide the round trips better than longer batches.
+// One workgroup per (token, block of 16 heads), one wave per head: lane l owns dims 8l .. 8l+7, so every
+// load and store of a row is contiguous across the wave. The splits are read four at a time with every
+// load of a batch issued before any is used (a token rarely has more than a few splits), so a merge
+// costs about one global round trip per batch.
+//
+// V4.1 instance: every token comes through, and each (head, 32-dim chunk) leaves as MXFP8 (vLLM
+// swapab_decode_attn step 9): x = the merged output (0 when the token has no rows or an infinite sink),
+// its dims 448..511 rotated back per GPT-J pair in fp32, then amax over the chunk (four lanes) =
+// max(max |x|, 1e-10), scale byte = ue8m0 of amax * (1/448) rounded up to a power of two, codes =
+// e4m3(x * 2^(127 - byte)) (v_cvt_pk_fp8_f32: round to nearest even; |x * 2^(127 - byte)| stays within
+// 448 up to one rounding of the product, which still rounds to 448).
 template <bool V41>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr bool v41 = V41;
+__global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
   const int t = blockIdx.x;
   const int s0 = p.num_splits[t];
   const int n = p.num_splits[t + 1] - s0;
-  if (n < (v41 ? 1 : 2)) return;
+  if (n < (V41 ? 1 : 2)) return;
   const int tid = threadIdx.x;
-  const int h = blockIdx.y * 16 + (tid >> 4);
-  const int d0 = 32 * (tid & 15);
+  const int lane = tid & 63;
+  const int h = blockIdx.y * 16 + (tid >> 6);
+  const int d0 = 8 * lane;
   const bool has_sink = p.sink != nullptr;
   const float sk = has_sink ? p.sink[h] : kNegInf;
-  uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + d0;
-  ChunkRope rope;
-  if constexpr (v41) rope.load(p, t, d0);
-  constexpr int KB = v41 ? 2 : 4;  // splits per batch
+  // V4.1: the cos / sin of the lane's four pairs, loaded before the merge so that their latency overlaps
+  // that of the partials (identity for a position outside the table)
+  f32x4 rc = f32x4{1.f, 1.f, 1.f, 1.f}, rs = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool rot = false;
+  if constexpr (V41) {
+    if (d0 >= 448) {
+      const int64_t pos = p.positions[t];
+      if (pos >= 0 && pos < p.num_positions) {
+        const float* cs = p.cos_sin + pos * p.cs_stride + (d0 - 448) / 2;  // pairs (d0 - 448) / 2 .. + 3
+        rc = *(const f32x4*)cs;
+        rs = *(const f32x4*)(cs + 32);
+        rot = true;
+      }
+    }
+  }
+  constexpr int KB = 4;  // splits per batch
   // running merge state: max M, denominator den and accumulator relative to M
   float M = sk;
   float den = has_sink ? 1.0f : 0.0f;  // exp(sk - M) with M = sk
-  f32x4 acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   for (int k0 = 0; k0 < n; k0 += KB) {
     float lk[KB];
-    f32x4 v[KB][8];
+    f32x4 v[KB][2];
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int k = k0 + j < n ? k0 + j : k0;  // a duplicate read beyond the end, weighted 0 below
       lk[j] = p.lse_acc[(int64_t)(s0 + k) * p.H + h];
       const f32x4* src = (const f32x4*)(p.o_acc + ((int64_t)(s0 + k) * p.H + h) * kDv + d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = src[e];
+      v[j][0] = src[0];
+      v[j][1] = src[1];
     }
     float bm = M;
 #pragma unroll
@@ -220,41 +172,67 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     const float r = (M == kNegInf) ? 0.f : expf(M - bm);  // rescale what was merged so far
     den *= r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= r;
+    acc[0] *= r;
+    acc[1] *= r;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const float wj = (k0 + j < n && lk[j] != kNegInf) ? expf(lk[j] - bm) : 0.f;
       den += wj;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wj * v[j][e];
+      acc[0] += wj * v[j][0];
+      acc[1] += wj * v[j][1];
     }
     M = bm;
   }
-  if constexpr (v41) {
-    const bool ok = !(M == kNegInf || M == kPosInf);
-    mxfp8_store(p, t, h, d0, ok, den, acc, rope);
-    if (p.lse && (tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = ok ? M + logf(den) : M;
+  const bool ok = !(M == kNegInf || M == kPosInf);
+  if constexpr (V41) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = ok ? acc[0][k] / den : 0.f;
+      x[4 + k] = ok ? acc[1][k] / den : 0.f;
+    }
+    if (rot) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float oe = x[2 * j], oo = x[2 * j + 1];
+        x[2 * j] = __builtin_fmaf(oe, rc[j], rs[j] * oo);
+        x[2 * j + 1] = __builtin_fmaf(oo, rc[j], -(rs[j] * oe));
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the chunk's four lanes
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, 1e-10f);
+    const uint32_t yb = __builtin_bit_cast(uint32_t, amax * (float)(1.0 / 448.0));
+    const uint32_t ex = ((yb >> 23) & 0xFFu) + ((yb & 0x7FFFFFu) != 0u ? 1u : 0u);
+    const float inv = __builtin_bit_cast(float, (254u - ex) << 23);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * inv, x[5] * inv, 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * inv, x[7] * inv, w1, true);
+    *(u32x2*)(p.o8 + (int64_t)t * p.o8_st + (int64_t)h * p.o8_sh + d0) = u32x2{(uint32_t)w0, (uint32_t)w1};
+    if ((lane & 3) == 0) p.osc[(int64_t)t * p.osc_st + (int64_t)h * p.osc_sh + (lane >> 2)] = (uint8_t)ex;
+    if (p.lse && lane == 0) p.lse[(int64_t)t * p.l_st + h] = ok ? M + logf(den) : M;
     return;
   }
-  if (M == kNegInf || M == kPosInf) {
-    for (int e = 0; e < 32; e += 8) *(u32x4*)(orow + e) = u32x4{0u, 0u, 0u, 0u};
-    if ((tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = M;
+  uint16_t* orow = p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + d0;
+  if (!ok) {
+    *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) p.lse[(int64_t)t * p.l_st + h] = M;
     return;
   }
   const float inv = 1.0f / den;
+  u32x4 o;
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4& a = acc[e + (q >> 1)];
-      const int k = (q & 1) * 2;
-      o[q] = (uint32_t)f32_to_bf16_bits(a[k] * inv) | ((uint32_t)f32_to_bf16_bits(a[k + 1] * inv) << 16);
-    }
-    *(u32x4*)(orow + 4 * e) = o;
+  for (int q = 0; q < 4; ++q) {
+    const f32x4& a = acc[q >> 1];
+    const int k = (q & 1) * 2;
+    o[q] = (uint32_t)f32_to_bf16_bits(a[k] * inv) | ((uint32_t)f32_to_bf16_bits(a[k + 1] * inv) << 16);
   }
-  if ((tid & 15) == 0) p.lse[(int64_t)t * p.l_st + h] = M + logf(den);
+  *(u32x4*)orow = o;
+  if (lane == 0) p.lse[(int64_t)t * p.l_st + h] = M + logf(den);
 }
 
 hipError_t launch_sched(const SchedParams& p, hipStream_t stream) {
@@ -265,9 +243,9 @@ hipError_t launch_sched(const SchedParams& p, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (p.o8)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T, p.H / 16), dim3(1024), 0, stream, p);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T, p.H / 16), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T, p.H / 16), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 
