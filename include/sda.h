@@ -230,7 +230,7 @@ typedef struct sda_v41 {
 } sda_v41;
 
 /* Host only. Workspace of sda_sparse_decode_attn_v41: that of sda_workspace_bytes(T, H, 512, plan)
- * plus the rotated q (bf16 [T][H][512]). */
+ * plus the rotated query dims 448..511 (bf16 [T][H][64]). */
 size_t sda_workspace_bytes_v41(int T, int H, const sda_plan* plan /*host*/);
 
 /* V4.1 decode: the arguments of sda_sparse_decode_attn with d_qk = d_v = 512, the bf16 output replaced

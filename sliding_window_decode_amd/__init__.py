@@ -254,7 +254,7 @@ class Decoder:
         self.meta = torch.empty((self.plan.num_parts, META_INTS), dtype=torch.int32, device=device)
         self.num_splits = torch.empty(T + 1, dtype=torch.int32, device=device)
         nbytes = workspace_bytes(T, H, 512, self.plan)
-        if d_qk == 512:  # room for the V4.1 call's rotated q as well
+        if d_qk == 512:  # room for the V4.1 call's rotated query dims as well
             nbytes = max(nbytes, workspace_bytes_v41(T, H, self.plan))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 

@@ -114,7 +114,7 @@ WorkspaceLayout layout_of(int T, int H, int d_v, int P) {
   w.num_splits = round_up(w.meta + (size_t)P * SDA_META_INTS * sizeof(int32_t), 256);
   w.total = round_up(w.num_splits + ((size_t)T + 1) * sizeof(int32_t), 256);
   w.q_rot = w.total;
-  w.total_v41 = round_up(w.q_rot + (size_t)T * H * 512 * sizeof(uint16_t), 256);
+  w.total_v41 = round_up(w.q_rot + (size_t)T * H * 64 * sizeof(uint16_t), 256);
   return w;
 }
 
@@ -547,9 +547,10 @@ int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stri
   rp.H = H;
   hipError_t e = sda::launch_rope_q(rp, st);
   if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
-  // decode on the rotated q, every token leaving as an fp32 partial
-  sda::DecodeParams p = decode_params(rp.q_out, (int64_t)H * 512, 512, T, H, cache, list, extra_cache, extra_list,
+  // decode on q with its rotated dims from the workspace, every token leaving as an fp32 partial
+  sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
                                       attn_sink, scale, meta, num_splits, ws, wl, nullptr, 0, 0, nullptr, 0);
+  p.q_rope = rp.q_out;
   p.all_partial = 1;
   e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, 512, plan->precision, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");

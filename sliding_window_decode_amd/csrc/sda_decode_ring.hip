@@ -191,8 +191,14 @@ void decode_ring_kernel(DecodeParams p) {
     const uint16_t* qh = p.q + (int64_t)t * p.q_st + (int64_t)(h0 + li) * p.q_sh + 16 * G;
 #pragma unroll
     for (int j = 0; j < NQJ; ++j) {
-      qreg[2 * j] = *(const bf16x8*)(qh + 64 * (qj0 + j));
-      qreg[2 * j + 1] = *(const bf16x8*)(qh + 64 * (qj0 + j) + 8);
+      const uint16_t* src = qh + 64 * (qj0 + j);
+      if constexpr (DQK == 512) {  // V4.1 calls: the rotated dims 448..511 from their own buffer
+        // (the lane's offset is recomputed here, behind an opaque zero, rather than kept live in the loop)
+        if (qj0 + j == 7 && p.q_rope)
+          src = p.q_rope + ((int64_t)t * p.H + h0) * 64 + (64 * li + 16 * G + opaque_lane_zero());
+      }
+      qreg[2 * j] = *(const bf16x8*)src;
+      qreg[2 * j + 1] = *(const bf16x8*)(src + 8);
     }
     if constexpr (kRope) {
 #pragma unroll

@@ -48,7 +48,9 @@ struct DecodeSmem {
   int slot_any[NSLOT];
 };
 
-template <int DQK, int NH2, int NTERM>
+// QR: built for V4.1 calls, whose query dims 448..511 come from the rotated buffer (a separate build, so
+// that the extra loads do not add to the register pressure of every other call)
+template <int DQK, int NH2, int NTERM, bool QR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH2 == 1 ? 3 : 1)))
 void decode_kernel(DecodeParams p) {
   constexpr int RS = DecodeSmem<DQK, NH2>::RS;
@@ -278,6 +280,16 @@ void decode_kernel(DecodeParams p) {
         const uint16_t* qh = qp + (int64_t)(h0 + 16 * hb + li) * p.q_sh;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
+        if constexpr (QR && !kRope) {
+          // V4.1 calls: dims 448..511 (wave 3, k-steps 2 and 3) from the rotated buffer [T][H][64]; the
+          // lane's offset is recomputed here, behind an opaque zero, rather than kept live in the loop
+          if (w == 3) {
+            const uint16_t* qr =
+                p.q_rope + ((int64_t)it0.t * p.H + h0 + 16 * hb) * 64 + (64 * li + 8 * G + opaque_lane_zero());
+            qreg[hb][2] = *(const bf16x8*)qr;
+            qreg[hb][3] = *(const bf16x8*)(qr + 32);
+          }
+        }
         if constexpr (kRope) qrope[hb] = *(const bf16x8*)(qh - 128 * w + 512 + 32 * (w & 1));
 #pragma unroll
         for (int db = 0; db < 8; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -459,16 +471,24 @@ void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int DQK, int NH2>
-static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
+template <int DQK, int NH2, bool QR>
+static hipError_t launch_decode_q(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * NH2));
   if (precision == 1)
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 1>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 1, QR>), grid, dim3(256), 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 2>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 2, QR>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 3>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 3, QR>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int DQK, int NH2>
+static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
+  if constexpr (DQK == 512) {
+    if (p.q_rope) return launch_decode_q<DQK, NH2, true>(p, num_parts, precision, stream);
+  }
+  return launch_decode_q<DQK, NH2, false>(p, num_parts, precision, stream);
 }
 
 hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,

@@ -31,6 +31,7 @@ struct ListDev {
 struct DecodeParams {
   const uint16_t* q;         // bf16 bits
   int64_t q_st, q_sh;        // element strides
+  const uint16_t* q_rope;    // V4.1 calls: dims 448..511 of q after RoPE, [T][H][64]; nullptr: from q
   uint16_t* out;             // bf16 bits
   int64_t o_st, o_sh;
   float* lse;
@@ -51,7 +52,7 @@ struct DecodeParams {
 struct RopeParams {
   const uint16_t* q;         // bf16 bits, [T][H][512] with strides
   int64_t q_st, q_sh;
-  uint16_t* q_out;           // [T][H][512] contiguous
+  uint16_t* q_out;           // dims 448..511 rotated, [T][H][64] contiguous
   const int64_t* positions;  // [T]
   const float* cos_sin;
   int64_t cs_stride, num_positions;

@@ -307,7 +307,7 @@ def test_v41_rejects_bad_arguments_on_the_host(kw, status):
 def test_v41_workspace_holds_the_rotated_q():
     plan = sda.sda_plan(64, 32, 2, 2)
     for T, H in ((1, 16), (256, 32), (64, 128)):
-        assert sda.workspace_bytes_v41(T, H, plan) >= sda.workspace_bytes(T, H, 512, plan) + T * H * 1024
+        assert sda.workspace_bytes_v41(T, H, plan) >= sda.workspace_bytes(T, H, 512, plan) + T * H * 128
     # the standard workspace is not enough for a V4.1 call
     with pytest.raises(sda.SdaError) as ei:
         _call_v41(ws_bytes=sda.workspace_bytes(4, 16, 512, sda.sda_plan(8, 16, 2, 2)))
