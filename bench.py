@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--parts", type=int, default=None)
     ap.add_argument("--heads-per-group", type=int, default=None)
     ap.add_argument("--fixed-overhead", type=int, default=None, help="override the plan's per-token tile overhead")
+    ap.add_argument("--schedule", choices=["auto", "split", "whole"], default="auto",
+                    help="split: scheduler + combine; whole: one workgroup per token; auto: whole when every "
+                         "token has the same tile count and T >= the split plan's parts (host-side lengths)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true", help="also time with rotating buffer sets larger than the MALL")
     ap.add_argument("--copy-calib", action="store_true",
@@ -200,6 +203,12 @@ def main():
         plan.heads_per_group = args.heads_per_group
     if args.fixed_overhead is not None:
         plan.fixed_overhead = args.fixed_overhead
+    # the caller's host-side lengths decide between the split schedule and one workgroup per token
+    qpl = max(1, getattr(w.lst, "queries_per_len", 1))
+    tiles = sda.token_tiles(w.lst.lens, w.lst.width, w.xlst.lens if w.xlst is not None else None, X, T=w.T,
+                            queries_per_len=qpl)
+    if args.schedule == "whole" or (args.schedule == "auto" and sda.whole_tokens_fits(plan, w.T, tiles)):
+        plan.whole_tokens = 1
     dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
     out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
@@ -210,15 +219,16 @@ def main():
         out8 = torch.empty((w.T, w.H, 512), dtype=torch.uint8, device="cuda")
         osc = torch.empty((w.T, w.H, 16), dtype=torch.uint8, device="cuda")
 
+    meta, num_splits = dec.sched_arrays  # None for a whole-token plan
+
     def step():
-        dec.schedule(dw.lst, dw.xlst)
+        dec.schedule(dw.lst, dw.xlst)  # nothing for a whole-token plan
         if v41:  # Q RoPE, decode, combine with the inverse RoPE and MXFP8 cast
             sda.sparse_decode_attn_v41(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
-                                       dec.meta, dec.num_splits, dec.workspace, dw.positions, dw.cos_sin, out8, osc,
-                                       lse)
+                                       meta, num_splits, dec.workspace, dw.positions, dw.cos_sin, out8, osc, lse)
         else:
             sda.sparse_decode_attn(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
-                                   dec.meta, dec.num_splits, dec.workspace, out, lse)
+                                   meta, num_splits, dec.workspace, out, lse)
 
     log(f"[bench] plan {plan}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -236,8 +246,8 @@ def main():
     # the decode kernel alone, back to back on the same stream, launched as in the step (V4.1: every token
     # leaves as a partial; the rotation of q changes values, not work)
     def decode_only():
-        sda.decode_splits(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan, dec.meta,
-                          dec.num_splits, dec.workspace, None if v41 else out, None if v41 else lse)
+        sda.decode_splits(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan, meta,
+                          num_splits, dec.workspace, None if v41 else out, None if v41 else lse)
 
     for _ in range(max(5, args.warmup // 2)):
         decode_only()
@@ -286,7 +296,8 @@ def main():
                    "extra_format": wl.FORMAT_NAMES[w.xcache.fmt] if w.xcache is not None else None,
                    "sink": w.sink is not None, "valid_rows": rows, "v41_rope_mxfp8_out": v41,
                    "plan": {"num_parts": plan.num_parts, "heads_per_group": plan.heads_per_group,
-                            "fixed_overhead": plan.fixed_overhead, "precision": plan.precision}},
+                            "fixed_overhead": plan.fixed_overhead, "precision": plan.precision,
+                            "whole_tokens": bool(plan.whole_tokens)}},
         "tflops": round(flops / t_step / 1e12, 2),
         "gbps": round(byts / t_step / 1e9, 1),
         "decode_kernel_us": round(ms_decode * 1e3, 2),
@@ -314,15 +325,15 @@ def main():
             sets.append((dw.q.clone(), c, xc, torch.empty_like(out), torch.empty_like(lse)))
         for i in range(nsets):
             q_, c_, xc_, o_, l_ = sets[i]
-            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, dec.meta,
-                                   dec.num_splits, dec.workspace, o_, l_)
+            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, meta,
+                                   num_splits, dec.workspace, o_, l_)
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(args.steps):
             q_, c_, xc_, o_, l_ = sets[i % nsets]
             dec.schedule(dw.lst, dw.xlst)
-            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, dec.meta,
-                                   dec.num_splits, dec.workspace, o_, l_)
+            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, meta,
+                                   num_splits, dec.workspace, o_, l_)
         e1.record(stream)
         torch.cuda.synchronize()
         ms_cold = e0.elapsed_time(e1) / args.steps

@@ -118,12 +118,24 @@ typedef struct sda_list {
  *                   which can move bf16 outputs of magnitude >= 2 by one ulp, 2^-6, more often than
  *                   the 1e-2 output tolerance allows), 2 = hi + lo terms (the default; ~2^-17), 3 =
  *                   three terms whose sum is P exactly (fp32-accurate). Terms multiply the P.V
- *                   matrix-core work. */
+ *                   matrix-core work.
+ *  whole_tokens     0 (what sda_make_plan sets): the scheduler cuts the (token, tile) sequence into
+ *                   num_parts parts of equal cost, splitting tokens across parts, and a combine merges
+ *                   the splits. 1: one workgroup per (token, head group) computes the token whole, in
+ *                   a grid of T x H/heads_per_group; no scheduler runs, no meta or num_splits array is
+ *                   read or written (callers pass NULL for both), no token is split and the plain call
+ *                   runs no combine (the V4.1 call still runs its epilogue). num_parts and
+ *                   fixed_overhead then only size the workspace. Results are the same either way; the
+ *                   whole-token plan saves two kernel launches per call and balances the GPU when every
+ *                   token has the same number of 64-row tiles (a full sliding window, a fixed top-k) and
+ *                   T x H/heads_per_group fills the GPU; with uneven tokens a part may wait for the
+ *                   longest. */
 typedef struct sda_plan {
   int32_t num_parts;
   int32_t heads_per_group;
   int32_t fixed_overhead;
   int32_t precision;
+  int32_t whole_tokens;
 } sda_plan;
 
 /* Size of one scheduler meta record, in int32 (meta is [num_parts][SDA_META_INTS]). */

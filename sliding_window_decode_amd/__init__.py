@@ -51,11 +51,13 @@ class sda_v41(ctypes.Structure):
 
 class sda_plan(ctypes.Structure):
     _fields_ = [("num_parts", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
-                ("fixed_overhead", ctypes.c_int32), ("precision", ctypes.c_int32)]
+                ("fixed_overhead", ctypes.c_int32), ("precision", ctypes.c_int32),
+                ("whole_tokens", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"sda_plan(num_parts={self.num_parts}, heads_per_group={self.heads_per_group}, "
-                f"fixed_overhead={self.fixed_overhead}, precision={self.precision})")
+                f"fixed_overhead={self.fixed_overhead}, precision={self.precision}, "
+                f"whole_tokens={self.whole_tokens})")
 
 
 _lib = None
@@ -147,6 +149,37 @@ def make_plan(T: int, H: int, d_qk: int, width: int, extra_width: int = 0, num_c
     plan = sda_plan()
     _check(lib().sda_make_plan(T, H, d_qk, width, extra_width, num_cus, ctypes.byref(plan)))
     return plan
+
+
+def token_tiles(lens, width: int, extra_lens=None, extra_width: int = 0, T: Optional[int] = None,
+                queries_per_len: int = 1):
+    """Host-side 64-row tile count of every token (numpy int array of length T): ceil(n / 64) per list with
+    n the length clamped to [0, width] (the width when lens is None), at least one tile per token. lens
+    holds one entry per queries_per_len consecutive tokens."""
+    import numpy as np
+
+    def per_list(ls, w):
+        if w <= 0:
+            return 0
+        if ls is None:
+            return np.full(T, (w + 63) // 64, dtype=np.int64)
+        n = np.clip(np.asarray(ls, dtype=np.int64), 0, w)
+        n = np.repeat(n, max(1, queries_per_len))[:T] if queries_per_len > 1 else n[:T]
+        return (n + 63) // 64
+
+    if T is None:
+        T = len(lens) * max(1, queries_per_len)
+    return np.maximum(per_list(lens, width) + per_list(extra_lens, extra_width), 1)
+
+
+def whole_tokens_fits(plan: sda_plan, T: int, tiles) -> bool:
+    """Caller policy for a whole-token plan: every token has the same tile count (so one workgroup per token
+    is balanced) and T, the whole-token grid's first dimension, is at least the split schedule's num_parts
+    (so the GPU is filled as well). Lengths are the caller's host-side knowledge (a full sliding window, a
+    fixed top-k); results do not depend on the choice."""
+    import numpy as np
+    tiles = np.asarray(tiles)
+    return tiles.size == T and T >= plan.num_parts and int(tiles.min()) == int(tiles.max())
 
 
 def workspace_bytes(T: int, H: int, d_v: int, plan: sda_plan) -> int:
@@ -259,7 +292,14 @@ class Decoder:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def schedule(self, lst: SlotList, extra: Optional[SlotList] = None, stream=None):
-        get_sched_meta(self.T, lst, extra, self.plan, self.meta, self.num_splits, stream)
+        """Runs the scheduler (nothing for a whole-token plan, which has no schedule)."""
+        if not self.plan.whole_tokens:
+            get_sched_meta(self.T, lst, extra, self.plan, self.meta, self.num_splits, stream)
+
+    @property
+    def sched_arrays(self):
+        """(meta, num_splits) to pass to the decode calls: None for a whole-token plan."""
+        return (None, None) if self.plan.whole_tokens else (self.meta, self.num_splits)
 
     def __call__(self, q, cache, lst, extra_cache=None, extra_lst=None, attn_sink=None, scale=None, out=None,
                  lse=None, schedule=True, stream=None):
@@ -272,8 +312,9 @@ class Decoder:
             lse = torch.empty((self.T, self.H), dtype=torch.float32, device=q.device)
         if schedule:
             self.schedule(lst, extra_lst, stream)
-        sparse_decode_attn(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, self.meta,
-                           self.num_splits, self.workspace, out, lse, stream)
+        meta, num_splits = self.sched_arrays
+        sparse_decode_attn(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, meta, num_splits,
+                           self.workspace, out, lse, stream)
         return out, lse
 
     def v41(self, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, positions, cos_sin, out_fp8=None,
@@ -288,6 +329,7 @@ class Decoder:
             lse = torch.empty((self.T, self.H), dtype=torch.float32, device=q.device)
         if schedule:
             self.schedule(lst, extra_lst, stream)
-        sparse_decode_attn_v41(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, self.meta,
-                               self.num_splits, self.workspace, positions, cos_sin, out_fp8, out_scale, lse, stream)
+        meta, num_splits = self.sched_arrays
+        sparse_decode_attn_v41(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, self.plan, meta, num_splits,
+                               self.workspace, positions, cos_sin, out_fp8, out_scale, lse, stream)
         return out_fp8, out_scale, lse

@@ -97,6 +97,8 @@ int check_plan(const sda_plan* plan, int H) {
   if (plan->fixed_overhead < 0 || plan->fixed_overhead > 1024)
     return fail(SDA_ERR_INVALID_ARG, "plan.fixed_overhead out of range");
   if (plan->precision < 1 || plan->precision > 3) return fail(SDA_ERR_INVALID_ARG, "plan.precision must be 1, 2 or 3");
+  if (plan->whole_tokens != 0 && plan->whole_tokens != 1)
+    return fail(SDA_ERR_INVALID_ARG, "plan.whole_tokens must be 0 or 1");
   return SDA_OK;
 }
 
@@ -242,6 +244,7 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   // long NVFP4 lists balance best when parts are cut by tiles alone (measured)
   plan->fixed_overhead = hb == 16 ? 0 : 2;
   plan->precision = 2;
+  plan->whole_tokens = 0;
   return SDA_OK;
 }
 
@@ -257,6 +260,7 @@ int sda_get_sched_meta(int T, const sda_list* list, const sda_list* extra, const
   if (rc) return rc;
   if (extra && (rc = check_list(extra, "extra"))) return rc;
   if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
+  if (plan->whole_tokens) return fail(SDA_ERR_INVALID_ARG, "a whole-token plan has no schedule");
   if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
   hipError_t e = sda::launch_sched(sched_params(T, list, extra, plan, meta, num_splits), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
@@ -269,6 +273,7 @@ int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens, int
   if (queries_per_len < 0) return fail(SDA_ERR_INVALID_ARG, "queries_per_len must be >= 0");
   const int div = queries_per_len > 1 ? queries_per_len : 1;
   if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
+  if (plan->whole_tokens) return fail(SDA_ERR_INVALID_ARG, "a whole-token plan has no schedule");
   if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
   const int P = plan->num_parts, F = plan->fixed_overhead;
   int64_t total = 0;
@@ -349,6 +354,8 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
   if ((rc = check_plan(plan, H))) return rc;
   if ((meta == nullptr) != (num_splits == nullptr))
     return fail(SDA_ERR_INVALID_ARG, "meta and num_splits must be given together");
+  if (plan->whole_tokens && meta)
+    return fail(SDA_ERR_INVALID_ARG, "a whole-token plan reads no meta or num_splits: pass NULL for both");
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
   if (!workspace || !aligned(workspace, 256)) return fail(SDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < (v41 ? wl.total_v41 : wl.total))
@@ -373,6 +380,9 @@ int check_v41(const sda_v41* v, int T, int H) {
   (void)H;
   return SDA_OK;
 }
+
+// Workgroups along the grid's first dimension: the scheduler's parts, or one per token (whole-token plans).
+int grid_parts(const sda_plan* plan, int T) { return plan->whole_tokens ? T : plan->num_parts; }
 
 sda::DecodeParams decode_params(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
                                 const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
@@ -444,13 +454,13 @@ int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
                              meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h, lse,
                              lse_stride_t, no_out);
   if (rc) return rc;
-  if (!meta) return fail(SDA_ERR_INVALID_ARG, "sda_decode_splits needs meta and num_splits");
+  if (!meta && !plan->whole_tokens) return fail(SDA_ERR_INVALID_ARG, "sda_decode_splits needs meta and num_splits");
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
   sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
                                       attn_sink, scale, meta, num_splits, (char*)workspace, wl, out, out_stride_t,
                                       out_stride_h, no_out ? nullptr : lse, lse_stride_t);
   p.all_partial = no_out ? 1 : 0;
-  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision,
+  hipError_t e = sda::launch_decode(p, grid_parts(plan, T), plan->heads_per_group, d_qk, plan->precision,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return SDA_OK;
@@ -469,7 +479,7 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
-  if (!meta) {
+  if (!meta && !plan->whole_tokens) {
     int32_t* m = (int32_t*)(ws + wl.meta);
     int32_t* ns = (int32_t*)(ws + wl.num_splits);
     hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
@@ -480,8 +490,9 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
   const sda::DecodeParams p = decode_params(q, q_stride_t, q_stride_h, T, H, cache, list, extra_cache, extra_list,
                                             attn_sink, scale, meta, num_splits, ws, wl, out, out_stride_t,
                                             out_stride_h, lse, lse_stride_t);
-  hipError_t e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, d_qk, plan->precision, st);
+  hipError_t e = sda::launch_decode(p, grid_parts(plan, T), plan->heads_per_group, d_qk, plan->precision, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (plan->whole_tokens) return SDA_OK;  // every token was written whole by the decode kernel
   e = sda::launch_combine(combine_params(T, H, p.o_acc, p.lse_acc, num_splits, attn_sink, out, out_stride_t,
                                          out_stride_h, lse, lse_stride_t),
                           st);
@@ -524,7 +535,7 @@ int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stri
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const WorkspaceLayout wl = layout_of(T, H, 512, plan->num_parts);
-  if (!meta) {
+  if (!meta && !plan->whole_tokens) {
     int32_t* m = (int32_t*)(ws + wl.meta);
     int32_t* ns = (int32_t*)(ws + wl.num_splits);
     hipError_t e = sda::launch_sched(sched_params(T, list, extra_list, plan, m, ns), st);
@@ -552,7 +563,7 @@ int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stri
                                       attn_sink, scale, meta, num_splits, ws, wl, nullptr, 0, 0, nullptr, 0);
   p.q_rope = rp.q_out;
   p.all_partial = 1;
-  e = sda::launch_decode(p, plan->num_parts, plan->heads_per_group, 512, plan->precision, st);
+  e = sda::launch_decode(p, grid_parts(plan, T), plan->heads_per_group, 512, plan->precision, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   // combine every token: merge, inverse RoPE, MXFP8
   sda::CombineParams c = combine_params(T, H, p.o_acc, p.lse_acc, num_splits, attn_sink, nullptr, 0, 0, lse,

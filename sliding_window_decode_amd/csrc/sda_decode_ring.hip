@@ -101,10 +101,8 @@ void decode_ring_kernel(DecodeParams p) {
 
   // list parameters are read from the kernel arguments where used (scalar loads), not held in registers
   auto LD = [&](int L) -> const ListDev& { return p.lst[L]; };
-  const int32_t* mt = p.meta + (int64_t)blockIdx.x * SDA_META_INTS;
   int32_t mrec[SDA_META_INTS];
-#pragma unroll
-  for (int i = 0; i < SDA_META_INTS; ++i) mrec[i] = mt[i];
+  part_record(p, mrec);
   const int bt = mrec[0], bi = mrec[1], et = mrec[2], ei = mrec[3], bk = mrec[4];
   if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
 

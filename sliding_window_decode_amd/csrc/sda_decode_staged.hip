@@ -65,7 +65,8 @@ void decode_kernel(DecodeParams p) {
   const ListDev lst0 = p.lst[0];
   const ListDev lst1 = p.lst[p.nlists > 1 ? 1 : 0];
   auto LD = [&](int L) -> const ListDev& { return L ? lst1 : lst0; };
-  const int32_t* mt = p.meta + (int64_t)blockIdx.x * SDA_META_INTS;
+  int32_t mt[SDA_META_INTS];
+  part_record(p, mt);
   const int bt = mt[0], bi = mt[1], et = mt[2], ei = mt[3], bk = mt[4];
   if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
 

@@ -70,6 +70,28 @@ __device__ __forceinline__ void gen_enter(ItemGen& g, const DecodeParams& p, Src
   if (t + 1 <= g.t_last && t + 1 < p.T) src.issue(p, t + 1);
 }
 
+// The part record of this workgroup (the layout gen_init reads): row blockIdx.x of the scheduler's meta
+// array, or, for a whole-token call (no meta array), token blockIdx.x from its first tile to its end,
+// with its clamped lengths read here (one dependent load, in place of the meta record's) and split
+// index blockIdx.x (used only when the token leaves as a partial).
+__device__ __forceinline__ void part_record(const DecodeParams& p, int32_t (&m)[SDA_META_INTS]) {
+  const int b = blockIdx.x;
+  if (p.meta) {
+    const int32_t* mt = p.meta + (int64_t)b * SDA_META_INTS;
+#pragma unroll
+    for (int i = 0; i < SDA_META_INTS; ++i) m[i] = mt[i];
+    return;
+  }
+  m[0] = b;
+  m[1] = 0;
+  m[2] = b + 1;
+  m[3] = 0;
+  m[4] = 0;
+  m[5] = b < p.T ? clamp_len(p.lst[0].lens, p.lst[0].lens_div, p.lst[0].width, b) : 0;
+  m[6] = (b < p.T && p.nlists > 1) ? clamp_len(p.lst[1].lens, p.lst[1].lens_div, p.lst[1].width, b) : 0;
+  m[7] = b;
+}
+
 // Starts at the part of meta record m (begin token, begin tile, end token, end tile, begin split,
 // clamped main and extra lengths of the begin token, num_splits[begin token]).
 template <class Src>

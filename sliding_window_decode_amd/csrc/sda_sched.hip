@@ -122,8 +122,9 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
 template <bool V41>
 __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
   const int t = blockIdx.x;
-  const int s0 = p.num_splits[t];
-  const int n = p.num_splits[t + 1] - s0;
+  // no num_splits array (a whole-token call): token t is its own single split, number t
+  const int s0 = p.num_splits ? p.num_splits[t] : t;
+  const int n = p.num_splits ? p.num_splits[t + 1] - s0 : 1;
   if (n < (V41 ? 1 : 2)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

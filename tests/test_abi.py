@@ -312,3 +312,42 @@ def test_v41_workspace_holds_the_rotated_q():
     with pytest.raises(sda.SdaError) as ei:
         _call_v41(ws_bytes=sda.workspace_bytes(4, 16, 512, sda.sda_plan(8, 16, 2, 2)))
     assert ei.value.status == sda.SDA_ERR_WORKSPACE
+
+
+def test_whole_token_plans_on_the_host():
+    """A whole-token plan takes no meta or num_splits, has no schedule, and whole_tokens is 0 or 1."""
+    T = 4
+    plan = sda.sda_plan(8, 16, 2, 3, 1)
+    q = _FakeTensor((T, 16, 512))
+    cache = sda.Cache(_FakeTensor((1,), 1 << 24), 16, 64, 64 * 528, sda.FP8_528, None)
+    lst = sda.SlotList(_FakeTensor((T, 128), 1 << 27), 128, None)
+    ws = _FakeTensor((1 << 30,), 1 << 30, itemsize=1)
+    with pytest.raises(sda.SdaError) as ei:
+        sda.sparse_decode_attn(q, cache, lst, None, None, None, 0.05, plan, _FakeTensor((8, 8), 1 << 34),
+                               _FakeTensor((T + 1,), 1 << 33), ws, _FakeTensor((T, 16, 512)),
+                               _FakeTensor((T, 16), itemsize=4), stream=0)
+    assert ei.value.status == sda.SDA_ERR_INVALID_ARG and b"whole-token" in sda.lib().sda_last_error()
+    with pytest.raises(sda.SdaError) as ei:
+        _call(plan=sda.sda_plan(8, 16, 2, 3, 2))
+    assert ei.value.status == sda.SDA_ERR_INVALID_ARG
+    with pytest.raises(sda.SdaError) as ei:
+        sda.get_sched_meta_host(T, np.full(T, 100, np.int32), 128, None, 0, plan)
+    assert ei.value.status == sda.SDA_ERR_INVALID_ARG
+    with pytest.raises(sda.SdaError) as ei:
+        sda.get_sched_meta(T, lst, None, plan, _FakeTensor((8, 8), 1 << 34), _FakeTensor((T + 1,), 1 << 33), 0)
+    assert ei.value.status == sda.SDA_ERR_INVALID_ARG
+    assert sda.make_plan(64, 128, 512, 128).whole_tokens == 0
+
+
+def test_whole_token_policy_helpers():
+    """token_tiles counts ceil(n / 64) per list (clamped lengths, widths when absent, at least one tile, lengths
+    per request repeated over their queries); whole_tokens_fits wants equal counts and T >= num_parts."""
+    tiles = sda.token_tiles(np.array([0, 1, 64, 65, 200, -3], np.int32), 128, None, 512)
+    assert list(tiles) == [8, 9, 9, 10, 10, 8]
+    assert list(sda.token_tiles(None, 2048, T=3)) == [32, 32, 32]
+    assert list(sda.token_tiles(np.array([0, 0], np.int32), 128)) == [1, 1]
+    assert list(sda.token_tiles(np.array([70, 10], np.int32), 128, T=5, queries_per_len=3)) == [2, 2, 2, 1, 1]
+    plan = sda.sda_plan(64, 32, 2, 2)
+    assert sda.whole_tokens_fits(plan, 64, np.full(64, 2))
+    assert not sda.whole_tokens_fits(plan, 63, np.full(63, 2))
+    assert not sda.whole_tokens_fits(plan, 64, np.r_[np.full(63, 2), 1])

@@ -433,3 +433,62 @@ def test_request_lengths_shared_by_queries(fmt, xfmt, H, qpl):
     _, out_g, lse_g = _run_cmp(g, f"grouped s_q={qpl}")
     out_e, lse_e, _ = DeviceWorkload(e).run()
     assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)
+
+
+# ------------------------------------------------------------------ whole-token plans (no scheduler, no combine)
+
+def _whole_plan(w):
+    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0)
+    plan.whole_tokens = 1
+    return plan
+
+
+@pytest.mark.parametrize("name", [n for n in wl.CONFIGS if n != "c8_v41_ue8m0"])
+def test_whole_token_plan_parity(name):
+    """One workgroup per (token, head group), no scheduler and no combine: the same bar against the oracle
+    on every kernel (ring and staged, every record format), with empty tokens (C1) and uneven lengths
+    (C3, C4)."""
+    w = wl.make_workload(name, seed=3, T=SMALL_T[name])
+    _log(f"[whole] {name} T={w.T}")
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    out, lse, dec = DeviceWorkload(w).run(plan=_whole_plan(w))
+    assert dec.plan.whole_tokens
+    info = compare(out, lse, o_ref, l_ref, what=f"{name} whole tokens")
+    _log(f"  {dec.plan} {info}")
+
+
+def test_whole_token_plan_equals_one_token_parts():
+    """Where the split schedule gives every part exactly one whole token (64 tokens of two tiles each over 64
+    parts at the 128-head SWA shape), the whole-token plan computes the same sums in the same order."""
+    w = wl.make_workload("c2_swa_h128", seed=0)
+    dw = DeviceWorkload(w)
+    o1, l1, d1 = dw.run()
+    assert not d1.plan.whole_tokens and d1.plan.num_parts == w.T
+    o2, l2, _ = dw.run(plan=_whole_plan(w))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_whole_token_plan_request_lengths_and_sinks():
+    """Lengths per request (queries_per_len = 3, ragged last request, empty requests) and infinite sinks on a
+    whole-token plan: bit-identical to the same lengths given per token, and within the bar of the oracle."""
+    qpl, T, H = 3, 13, 32
+    w = wl.small_workload(97, wl.FP8_528, wl.FP8_528, T=T, H=H, width=128, xwidth=320, num_slots=4096, sink=True,
+                          p_invalid=0.05, lens_lo=0)
+    rng = np.random.default_rng(5)
+    nreq = -(-T // qpl)
+    g = copy.deepcopy(w)
+    for L in (g.lst, g.xlst):
+        L.lens = rng.integers(0, L.width + 1, size=nreq).astype(np.int32)
+        L.lens[1] = 0  # an empty request
+        L.queries_per_len = qpl
+    g.sink[3] = np.inf
+    e = copy.deepcopy(g)
+    r = np.arange(T) // qpl
+    e.lst.lens = g.lst.lens[r].copy()
+    e.xlst.lens = g.xlst.lens[r].copy()
+    e.lst.queries_per_len = e.xlst.queries_per_len = 1
+    o_ref, l_ref = oracle.attention(g, nthreads=8)
+    out_g, lse_g, _ = DeviceWorkload(g).run(plan=_whole_plan(g))
+    compare(out_g, lse_g, o_ref, l_ref, what="whole tokens, request lengths")
+    out_e, lse_e, _ = DeviceWorkload(e).run(plan=_whole_plan(e))
+    assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+import sliding_window_decode_amd as sda
 import workloads as wl
 from gpu_util import DeviceWorkload, compare_v41
 
@@ -124,3 +125,15 @@ def test_v41_workload_full_size_sampled():
     compare_v41(c[ti], s[ti], l[ti], np.concatenate([r[0] for r in refs]), np.concatenate([r[1] for r in refs]),
                 np.concatenate([r[2] for r in refs]), what=f"c8 tokens {list(toks)}")
     _log(f"  {dec.plan} checked tokens {list(toks)}")
+
+
+def test_v41_whole_token_plan():
+    """The V4.1 call on a whole-token plan (no scheduler; the epilogue merges each token's single partial)."""
+    w = wl.make_workload("c8_v41_ue8m0", seed=4, T=12)
+    codes, scales, lse, _ = oracle.attention_v41(w, nthreads=8)
+    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width)
+    plan.whole_tokens = 1
+    c, s, l, dec = DeviceWorkload(w).run_v41(plan=plan)
+    assert dec.plan.whole_tokens
+    info = compare_v41(c, s, l, codes, scales, lse, what="c8 whole tokens")
+    _log(f"  {dec.plan} {info}")
