@@ -492,3 +492,16 @@ def test_whole_token_plan_request_lengths_and_sinks():
     compare(out_g, lse_g, o_ref, l_ref, what="whole tokens, request lengths")
     out_e, lse_e, _ = DeviceWorkload(e).run(plan=_whole_plan(e))
     assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)
+
+
+def test_whole_token_plan_decode_only_entry_point():
+    """sda_decode_splits on a whole-token plan (no meta, no num_splits) writes exactly what the whole op writes."""
+    w = wl.make_workload("c5_topk_v32", seed=2, T=SMALL_T["c5_topk_v32"])
+    dw = DeviceWorkload(w)
+    plan = _whole_plan(w)
+    o1, l1, dec = dw.run(plan=plan)
+    o2 = torch.full_like(o1, 7.0)
+    l2 = torch.full_like(l1, 7.0)
+    sda.decode_splits(dw.q, dw.cache, dw.lst, None, None, dw.sink, w.scale, dec.plan, None, None, dec.workspace, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
