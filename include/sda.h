@@ -163,14 +163,14 @@ size_t sda_workspace_bytes(int T, int H, int d_v, const sda_plan* plan /*host*/)
  * num_splits[begin_token]; parts with no tiles hold {T, 0, T, 0, 0, 0, 0, 0}) and
  * num_splits [T+1] int32, the exclusive prefix sum of the number of parts that touch each token.
  * The result depends only on the lengths, so one call can serve every layer of a decode step.
- * extra may be NULL. */
+ * extra may be NULL. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG. */
 int sda_get_sched_meta(int T, const sda_list* list /*host*/, const sda_list* extra /*host, nullable*/,
                        const sda_plan* plan /*host*/, int32_t* meta, int32_t* num_splits, void* stream);
 
 /* Host only. The same schedule as sda_get_sched_meta, computed on the calling thread from host
  * copies of the lengths (lens / extra_lens: one int32 per queries_per_len tokens, as in sda_list, or
  * NULL = width) into host arrays meta [num_parts][SDA_META_INTS] and num_splits [T+1]. For callers
- * that keep lengths on the host. */
+ * that keep lengths on the host. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG. */
 int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens /*host, nullable*/, int width,
                             const int32_t* extra_lens /*host, nullable*/, int extra_width /*0 = no extra list*/,
                             const sda_plan* plan /*host*/, int32_t* meta /*host*/, int32_t* num_splits /*host*/);
@@ -185,7 +185,8 @@ int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens /*ho
  *             softmax denominator and nothing to the numerator (vLLM swapab_decode_attn, step 9).
  *  scale      softmax scale applied to q.k (e.g. 1/sqrt(d_qk)).
  *  meta/num_splits  from sda_get_sched_meta with the same plan and lengths, or both NULL to have this
- *             call run the scheduler into the workspace first.
+ *             call run the scheduler into the workspace first; both NULL for a whole-token plan
+ *             (plan->whole_tokens), which runs neither the scheduler nor the combine.
  *  workspace  >= sda_workspace_bytes(T, H, d_v, plan) bytes, 256-byte aligned.
  *  out        bf16 [T][H][d_v]; element (t, h, d) at out[t*out_stride_t + h*out_stride_h + d],
  *             strides multiples of 8 elements, 16-byte aligned.
@@ -201,7 +202,9 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
                            void* stream);
 
 /* The decode kernel alone (FlashMLA sparse_decode.h: impl->run, before the combine): same arguments
- * and checks as sda_sparse_decode_attn, but meta and num_splits are required and no combine runs.
+ * and checks as sda_sparse_decode_attn, but meta and num_splits are required (NULL for a whole-token
+ * plan, whose tokens are all touched by a single workgroup, token t's partial going to split t) and
+ * no combine runs.
  * Tokens touched by a single part get their final out/lse rows; the others get normalized fp32
  * partials in the workspace (o_accum at offset 0, lse_accum after it, as laid out by
  * sda_workspace_bytes) for a later sda_combine_splits. With out NULL (lse then unused) every token
@@ -247,7 +250,8 @@ size_t sda_workspace_bytes_v41(int T, int H, const sda_plan* plan /*host*/);
 
 /* V4.1 decode: the arguments of sda_sparse_decode_attn with d_qk = d_v = 512, the bf16 output replaced
  * by `v41` (host descriptor, device buffers) and lse optional (NULL: not written). Every token passes
- * through the combine, where the output cast happens. Errors as sda_sparse_decode_attn, plus
+ * through the combine, where the output cast happens (with a whole-token plan: no scheduler, and the
+ * combine takes token t's single partial from split t). Errors as sda_sparse_decode_attn, plus
  * SDA_ERR_INVALID_ARG for a bad v41 descriptor. */
 int sda_sparse_decode_attn_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H,
                                const sda_cache* cache /*host*/, const sda_list* list /*host*/,
