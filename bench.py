@@ -165,8 +165,8 @@ def main():
     ap.add_argument("--heads-per-group", type=int, default=None)
     ap.add_argument("--fixed-overhead", type=int, default=None, help="override the plan's per-token tile overhead")
     ap.add_argument("--schedule", choices=["auto", "split", "whole"], default="auto",
-                    help="split: scheduler + combine; whole: one workgroup per token; auto: whole when every "
-                         "token has the same tile count and T >= the split plan's parts (host-side lengths)")
+                    help="split: scheduler + combine; whole: one workgroup per token; auto: whole when its "
+                         "makespan in tiles (host-side lengths) is close enough to the split plan's")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true", help="also time with rotating buffer sets larger than the MALL")
     ap.add_argument("--copy-calib", action="store_true",
@@ -207,7 +207,8 @@ def main():
     qpl = max(1, getattr(w.lst, "queries_per_len", 1))
     tiles = sda.token_tiles(w.lst.lens, w.lst.width, w.xlst.lens if w.xlst is not None else None, X, T=w.T,
                             queries_per_len=qpl)
-    if args.schedule == "whole" or (args.schedule == "auto" and sda.whole_tokens_fits(plan, w.T, tiles)):
+    v41 = w.rope is not None
+    if args.schedule == "whole" or (args.schedule == "auto" and sda.whole_tokens_fits(plan, w.T, tiles, v41)):
         plan.whole_tokens = 1
     dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
     out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")

@@ -172,14 +172,25 @@ def token_tiles(lens, width: int, extra_lens=None, extra_width: int = 0, T: Opti
     return np.maximum(per_list(lens, width) + per_list(extra_lens, extra_width), 1)
 
 
-def whole_tokens_fits(plan: sda_plan, T: int, tiles) -> bool:
-    """Caller policy for a whole-token plan: every token has the same tile count (so one workgroup per token
-    is balanced) and T, the whole-token grid's first dimension, is at least the split schedule's num_parts
-    (so the GPU is filled as well). Lengths are the caller's host-side knowledge (a full sliding window, a
-    fixed top-k); results do not depend on the choice."""
+def whole_tokens_fits(plan: sda_plan, T: int, tiles, v41: bool = False) -> bool:
+    """Caller policy for a whole-token plan, from host-side tile counts (token_tiles): compares the
+    makespans of the two schedules in 64-row tiles. One workgroup per token takes about the longest
+    token (or the even share sum / num_parts once tokens outnumber the split plan's parts); the split
+    plan takes about (sum + T x fixed overhead) / num_parts and two more launches (scheduler
+    and combine; only the scheduler for the V4.1 call, which still merges in its epilogue), each worth
+    about a tile. The whole-token plan is chosen while its makespan is within 1.3x the split one plus
+    two tiles (1.0x plus one for V4.1): measured on MI355X, it wins where tokens are equal or a few
+    tiles apart (the split plan also pays its partial writes and token switches) and loses where one
+    long token leaves the GPU idle. Results do not depend on the choice."""
     import numpy as np
-    tiles = np.asarray(tiles)
-    return tiles.size == T and T >= plan.num_parts and int(tiles.min()) == int(tiles.max())
+    tiles = np.asarray(tiles, dtype=np.int64)
+    if tiles.size != T or T < 1:
+        return False
+    total = int(tiles.sum())
+    whole = max(int(tiles.max()), -(-total // plan.num_parts))
+    split = (total + T * plan.fixed_overhead) / plan.num_parts
+    ratio, slack = (1.0, 1.0) if v41 else (1.3, 2.0)
+    return whole <= ratio * split + slack
 
 
 def workspace_bytes(T: int, H: int, d_v: int, plan: sda_plan) -> int:

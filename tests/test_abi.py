@@ -341,13 +341,23 @@ def test_whole_token_plans_on_the_host():
 
 def test_whole_token_policy_helpers():
     """token_tiles counts ceil(n / 64) per list (clamped lengths, widths when absent, at least one tile, lengths
-    per request repeated over their queries); whole_tokens_fits wants equal counts and T >= num_parts."""
+    per request repeated over their queries); whole_tokens_fits compares the two schedules' makespans."""
     tiles = sda.token_tiles(np.array([0, 1, 64, 65, 200, -3], np.int32), 128, None, 512)
     assert list(tiles) == [8, 9, 9, 10, 10, 8]
     assert list(sda.token_tiles(None, 2048, T=3)) == [32, 32, 32]
     assert list(sda.token_tiles(np.array([0, 0], np.int32), 128)) == [1, 1]
     assert list(sda.token_tiles(np.array([70, 10], np.int32), 128, T=5, queries_per_len=3)) == [2, 2, 2, 1, 1]
-    plan = sda.sda_plan(64, 32, 2, 2)
-    assert sda.whole_tokens_fits(plan, 64, np.full(64, 2))
-    assert not sda.whole_tokens_fits(plan, 63, np.full(63, 2))
-    assert not sda.whole_tokens_fits(plan, 64, np.r_[np.full(63, 2), 1])
+    # equal tokens, one per part: whole
+    assert sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 64, np.full(64, 2))
+    # a handful of tokens on a GPU-wide split plan: the two launches outweigh one extra tile
+    assert sda.whole_tokens_fits(sda.sda_plan(768, 16, 0, 2), 4, np.array([2, 1, 2, 2]))
+    # tokens a few tiles apart (2..10, as the SWA + extra-list shape): whole for the plain call, split for V4.1
+    t = np.r_[np.full(128, 10), np.full(128, 2)]
+    assert sda.whole_tokens_fits(sda.sda_plan(256, 32, 2, 2), 256, t)
+    assert not sda.whole_tokens_fits(sda.sda_plan(256, 32, 2, 2), 256, t, v41=True)
+    # one long token per workgroup against balanced parts (2..34 tiles over 768 parts): split
+    t = np.r_[np.full(256, 34), np.full(256, 2)]
+    assert not sda.whole_tokens_fits(sda.sda_plan(768, 16, 0, 2), 512, t)
+    # more tokens than parts: the even share bounds the whole-token makespan
+    assert sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 640, np.full(640, 2))
+    assert not sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 63, np.full(64, 2))
