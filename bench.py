@@ -210,6 +210,9 @@ def main():
     v41 = w.rope is not None
     if args.schedule == "whole" or (args.schedule == "auto" and sda.whole_tokens_fits(plan, w.T, tiles, v41)):
         plan.whole_tokens = 1
+        if args.heads_per_group is None:
+            plan.heads_per_group = sda.whole_token_heads_per_group(
+                plan, w.T, w.H, w.d_qk, [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None])
     dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
     out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")

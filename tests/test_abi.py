@@ -361,3 +361,15 @@ def test_whole_token_policy_helpers():
     # more tokens than parts: the even share bounds the whole-token makespan
     assert sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 640, np.full(640, 2))
     assert not sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 63, np.full(64, 2))
+
+
+def test_whole_token_heads_per_group():
+    """16-head workgroups for whole-token calls on the fp8 ring kernel when they fit one round of two per CU."""
+    p32 = sda.sda_plan(64, 32, 2, 2, 1)
+    assert sda.whole_token_heads_per_group(p32, 64, 128, 512, [sda.FP8_SLOTSCALE, None]) == 16
+    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_528, sda.FP8_528]) == 16
+    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.MODEL1_584, sda.MODEL1_584]) == 32  # staged kernel
+    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_528, sda.NVFP4_288]) == 32
+    assert sda.whole_token_heads_per_group(p32, 512, 32, 512, [sda.FP8_528, None]) == 32  # two rounds
+    p64 = sda.sda_plan(128, 64, 2, 2, 1)
+    assert sda.whole_token_heads_per_group(p64, 128, 128, 576, [sda.V32_656, None]) == 64

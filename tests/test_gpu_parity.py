@@ -457,6 +457,21 @@ def test_whole_token_plan_parity(name):
     _log(f"  {dec.plan} {info}")
 
 
+@pytest.mark.parametrize("name", ["c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c6_swa_ue8m0"])
+def test_whole_token_plan_16_head_groups(name):
+    """The head grouping the binding picks for whole-token calls on the fp8 ring kernel (16 heads per
+    workgroup): same bar against the oracle."""
+    w = wl.make_workload(name, seed=4, T=SMALL_T[name])
+    plan = _whole_plan(w)
+    plan.heads_per_group = sda.whole_token_heads_per_group(
+        plan, w.T, w.H, w.d_qk, [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None])
+    assert plan.heads_per_group == 16
+    _log(f"[whole hb16] {name} T={w.T}")
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    out, lse, dec = DeviceWorkload(w).run(plan=plan)
+    compare(out, lse, o_ref, l_ref, what=f"{name} whole tokens, 16 heads per group")
+
+
 def test_whole_token_plan_equals_one_token_parts():
     """Where the split schedule gives every part exactly one whole token (64 tokens of two tiles each over 64
     parts at the 128-head SWA shape), the whole-token plan computes the same sums in the same order."""
