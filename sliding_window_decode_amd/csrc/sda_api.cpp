@@ -146,9 +146,10 @@ hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_gro
   const bool fp4 = p.lst[0].format == SDA_NVFP4_288 || (p.nlists > 1 && p.lst[1].format == SDA_NVFP4_288);
   // the ring kernel takes FP8_UE8M0 lists only when every list is one
   const int ue = (p.lst[0].format == SDA_FP8_UE8M0) + (p.nlists > 1 && p.lst[1].format == SDA_FP8_UE8M0);
-  // MODEL1_584 rows hold bf16 value dims, which the register-staged kernel's bf16 tile takes as they are
-  const bool m1 = p.lst[0].format == SDA_MODEL1_584 || (p.nlists > 1 && p.lst[1].format == SDA_MODEL1_584);
-  const bool staged = fp4 || m1 || (ue > 0 && ue < p.nlists);
+  // MODEL1_584 lists: the ring kernel when every list is one and a workgroup takes 32 or more heads (its
+  // 592-byte ring rows leave no room for two 16-head workgroups per CU), else the staged kernel
+  const int m1 = (p.lst[0].format == SDA_MODEL1_584) + (p.nlists > 1 && p.lst[1].format == SDA_MODEL1_584);
+  const bool staged = fp4 || (m1 > 0 && (m1 < p.nlists || heads_per_group < 32)) || (ue > 0 && ue < p.nlists);
   // the register-staged kernel takes at most 32 heads per workgroup
   return staged ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision,
                                        stream)

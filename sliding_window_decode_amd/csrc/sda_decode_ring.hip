@@ -1,6 +1,6 @@
-// sda_decode_ring.hip -- split-KV decode attention over fp8 caches (per-slot scale, 528-byte and
-// 656-byte records) for gfx950, with the gathered records streamed into an LDS ring by direct
-// global -> LDS loads.
+// sda_decode_ring.hip -- split-KV decode attention over fp8 caches (per-slot scale, 528-byte,
+// 656-byte and 584-byte MODEL1 records) for gfx950, with the gathered records streamed into an LDS
+// ring by direct global -> LDS loads.
 //
 // Workgroup = one scheduler part x HS sets of 16 query heads, 4 HS waves; a part is a run of (token,
 // 64-row tile) items. The records of a tile land, as raw bytes, in one of NB LDS ring buffers whose
@@ -60,16 +60,23 @@ struct RingShape {
   static constexpr int NPART = kDimSplit ? 2 : 1;  // partial score arrays
 };
 
-template <int DQK, int HS, int NB, bool UE>
+// Record kinds of a ring kernel build: the fp8 formats with fp32 scales (per slot or per 128 dims), FP8_UE8M0
+// (a power-of-two scale per 32 dims) and MODEL1_584 (448 fp8 dims with a power-of-two scale per 64 dims,
+// then 64 bf16 dims).
+enum RingKind { kRingF32Scales = 0, kRingUe8m0 = 1, kRingModel1 = 2 };
+
+template <int DQK, int HS, int NB, int FK>
 struct RingSmem {
-  static constexpr int RS = DQK == 576 ? 656 : 528;  // ring row stride in bytes (odd number of chunks)
+  // ring row stride in bytes (odd number of chunks); a MODEL1_584 row holds the record's 576 bytes of
+  // codes and bf16 values, then its bytes 568..583 (the scales at row bytes 584..590)
+  static constexpr int RS = DQK == 576 ? 656 : (FK == kRingModel1 ? 592 : 528);
   static constexpr int NW = RingShape<HS>::NW;
   char ring[NB][kTileRows * RS];
   f32x4 sx[RingShape<HS>::NPART][HS][4][64];  // (partial) scores per 16-row block and head set, MFMA layout
   float sscale[NB][64];         // per-slot scales (FP8_SLOTSCALE)
   // per scale group: its scale for every row of the tile (128-dim groups; the ue8m0 format's 32-dim
   // groups in the kernels built for it)
-  float vs[UE ? 16 : 4][64];
+  float vs[FK == kRingUe8m0 ? 16 : (FK == kRingModel1 ? 8 : 4)][64];
   uint32_t vmask[NB][NW];       // valid rows of each ring buffer, one mask per gathering wave
   uint64_t raddr[NW][RingShape<HS>::RW];  // per wave: record addresses of the rows it gathers
 };
@@ -78,11 +85,11 @@ struct RingSmem {
 // k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'. UE: built for calls whose
 // lists are all FP8_UE8M0 (512 dims), and only for them (carrying both decodings raises the register
 // pressure of every call; calls that mix it with another format run the staged kernel).
-template <int DQK, int HS, int NTERM, int NB, bool UE>
+template <int DQK, int HS, int NTERM, int NB, int FK>
 __global__ __launch_bounds__(64 * RingShape<HS>::NW)
 __attribute__((amdgpu_waves_per_eu(RingShape<HS>::NW == 8 || (DQK == 512 && NB == 2) ? 2 : 1)))
 void decode_ring_kernel(DecodeParams p) {
-  using Smem = RingSmem<DQK, HS, NB, UE>;
+  using Smem = RingSmem<DQK, HS, NB, FK>;
   using Shape = RingShape<HS>;
   constexpr int RS = Smem::RS;
   constexpr int RSC = RS / 16;                // chunks per ring row
@@ -90,7 +97,8 @@ void decode_ring_kernel(DecodeParams p) {
   constexpr int NRB = Shape::NRB, NDG = Shape::NDG;
   constexpr int NI = (RW * RSC + 63) / 64;    // gather instructions per wave and tile
   constexpr bool kRope = DQK == 576;
-  constexpr bool kUe8m0 = UE && DQK == 512;  // FP8_UE8M0 records hold 512 dims
+  constexpr bool kUe8m0 = FK == kRingUe8m0 && DQK == 512;  // FP8_UE8M0 records hold 512 dims
+  constexpr bool kM1 = FK == kRingModel1 && DQK == 512;    // MODEL1_584 records
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -143,7 +151,10 @@ void decode_ring_kernel(DecodeParams p) {
     for (int i = 0; i < NI; ++i) {
       const int c = 64 * i + lane;
       const int rl = c / RSC, ch = c - rl * RSC;
-      src[i] = sm.raddr[w][rl % RW] + 16 * (ch < nch ? ch : 0);
+      if constexpr (kM1)
+        src[i] = sm.raddr[w][rl % RW] + (ch < 36 ? 16 * ch : 568);
+      else
+        src[i] = sm.raddr[w][rl % RW] + 16 * (ch < nch ? ch : 0);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -342,8 +353,13 @@ void decode_ring_kernel(DecodeParams p) {
           // valid rows of the block: gathered by one wave (16 rows each) or two (8 rows each)
           const uint32_t vmw = RW == 16 ? sm.vmask[b][blk] : (sm.vmask[b][2 * blk] | (sm.vmask[b][2 * blk + 1] << 8));
           const uint32_t blk_off = (uint32_t)(16 * blk * RS);
-          u32x4 sb = u32x4{0u, 0u, 0u, 0u};  // the row's 16 ue8m0 bytes
-          if constexpr (SCALED) sb = *(const u32x4*)(ring + (16 * blk + li) * RS + 512);
+          u32x4 sb = u32x4{0u, 0u, 0u, 0u};  // the row's 16 ue8m0 bytes (MODEL1_584: its 7 in words 0, 1)
+          if constexpr (kM1) {
+            const u32x2 b8 = *(const u32x2*)(ring + (16 * blk + li) * RS + 584);
+            sb = u32x4{b8[0], b8[1], 0u, 0u};
+          } else if constexpr (SCALED) {
+            sb = *(const u32x4*)(ring + (16 * blk + li) * RS + 512);
+          }
           f32x4 acc[QG];
           f32x4 accr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -354,12 +370,21 @@ void decode_ring_kernel(DecodeParams p) {
 #pragma unroll
             for (int g = 0; g < QG; ++g) x[g] = *(const u32x4*)(ring + qk_off + blk_off + 64 * (2 * (g0 + g) + half));
             // each fragment is widened right before its two products (short-lived temporaries); its 16
-            // dims 64 (2 (g0+g) + half) + 16G .. lie in 32-dim group 4 (g0+g) + 2 half + G / 2
+            // dims 64 (2 (g0+g) + half) + 16G .. lie in 32-dim group 4 (g0+g) + 2 half + G / 2 (64-dim
+            // group 2 (g0+g) + half)
 #pragma unroll
             for (int g = 0; g < QG; ++g) {
-              const float cs = SCALED ? ue8m0_scale(sb[g0 + g] >> (8 * (2 * half + (G >> 1)))) : 1.0f;
+              const int j64 = 2 * (g0 + g) + half;
               bf16x8 lo, hi;
-              e4m3x16_to_bf16_scaled(x[g], cs, lo, hi);
+              if (kM1 && j64 == 7) {  // MODEL1_584 dims 448..511: bf16 values at row byte 448 + 2 (dim - 448)
+                const char* rb = ring + qk_off + blk_off - 16 * G + 448 + 32 * G;
+                lo = *(const bf16x8*)rb;
+                hi = *(const bf16x8*)(rb + 16);
+              } else {
+                const float cs = kM1 ? ue8m0_scale(sb[j64 >> 2] >> (8 * (j64 & 3)))
+                                 : SCALED ? ue8m0_scale(sb[g0 + g] >> (8 * (2 * half + (G >> 1)))) : 1.0f;
+                e4m3x16_to_bf16_scaled(x[g], cs, lo, hi);
+              }
               acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qreg[2 * (2 * g + half)], acc[g], 0, 0, 0);
               acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qreg[2 * (2 * g + half) + 1], acc[g], 0, 0, 0);
             }
@@ -376,7 +401,7 @@ void decode_ring_kernel(DecodeParams p) {
             const f32x4 ss = *(const f32x4*)&sm.sscale[b][16 * blk + 4 * G];
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[r] = f32x4{ss[r], ss[r], ss[r], ss[r]};
-          } else if (SCALED) {
+          } else if (SCALED || kM1) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[r] = f32x4{1.f, 1.f, 1.f, 1.f};
           } else {
@@ -400,7 +425,15 @@ void decode_ring_kernel(DecodeParams p) {
         qk_blocks(std::false_type{});
       // the scale of each of this wave's dim groups for every row (PV of all head sets)
       if (hs == 0 && !slot_scaled) {
-        if constexpr (kUe8m0) {
+        if constexpr (kM1) {
+#pragma unroll
+          for (int dg = 0; dg < NDG; ++dg) {  // the group's two 64-dim scales (the bf16 dims: 1)
+            const int gi = NDG * sub + dg;
+            const uint32_t wd = *(const uint16_t*)(ring + lane * RS + 584 + 2 * gi);
+            sm.vs[2 * gi][lane] = ue8m0_scale(wd);
+            sm.vs[2 * gi + 1][lane] = gi == 3 ? 1.0f : ue8m0_scale(wd >> 8);
+          }
+        } else if constexpr (kUe8m0) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
             const uint32_t wd = *(const uint32_t*)(ring + vs_off + 4 * dg);  // the group's 4 ue8m0 bytes
@@ -496,6 +529,68 @@ void decode_ring_kernel(DecodeParams p) {
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
         const uint32_t vaddr = lds_u32(ring) + pv_off + 128 * dg;
+        if constexpr (kM1) {
+          // MODEL1_584: one P' per 64 dims, in four quarters of 2 dim blocks; the last two quarters of
+          // dim group 3 (dims 448..511) are bf16 values, read transposed 16 bits at a time: lane (li, G)
+          // points at row 32 kk + 8 G + li / 4 (+ 4), dims 16 li % 4 .. + 3 of its block, and receives
+          // dim li of the group's four rows
+          const int gi = NDG * sub + dg;
+          const uint32_t baddr = lds_u32(ring) + (uint32_t)((8 * G + (li >> 2)) * RS + 448 + 8 * (li & 3));
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            bf16x8 A[2][NTERM];
+            make_p(sm.vs[2 * gi + h2], A);
+            if (gi == 3 && h2 == 1) {
+              i32x2 y[4][2][2];  // [dim block][kk][rows +0 / +4]
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                  y[d][kk][0] = lds_tr16(baddr + 32 * kk * RS + 32 * d);
+                  y[d][kk][1] = lds_tr16(baddr + (32 * kk + 4) * RS + 32 * d);
+                }
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)"
+                           : "+v"(y[0][0][0]), "+v"(y[0][0][1]), "+v"(y[0][1][0]), "+v"(y[0][1][1]),
+                             "+v"(y[1][0][0]), "+v"(y[1][0][1]), "+v"(y[1][1][0]), "+v"(y[1][1][1]),
+                             "+v"(y[2][0][0]), "+v"(y[2][0][1]), "+v"(y[2][1][0]), "+v"(y[2][1][1]),
+                             "+v"(y[3][0][0]), "+v"(y[3][0][1]), "+v"(y[3][1][0]), "+v"(y[3][1][1]));
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                  const bf16x8 B = __builtin_bit_cast(
+                      bf16x8, u32x4{(uint32_t)y[d][kk][0][0], (uint32_t)y[d][kk][0][1], (uint32_t)y[d][kk][1][0],
+                                    (uint32_t)y[d][kk][1][1]});
+                  f32x4& o = O[8 * dg + 4 + d];
+#pragma unroll
+                  for (int t = 0; t < NTERM; ++t) o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk][t], B, o, 0, 0, 0);
+                }
+              }
+              continue;
+            }
+            i32x2 x[4][2];  // [dim block][kk]
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) x[d][kk] = lds_tr8(vaddr + 32 * kk * RS + 16 * (4 * h2 + d));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[1][0]), "+v"(x[1][1]), "+v"(x[2][0]),
+                           "+v"(x[2][1]), "+v"(x[3][0]), "+v"(x[3][1]));
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                const bf16x8 B = e4m3x8_to_bf16(x[d][kk]);
+                f32x4& o = O[8 * dg + 4 * h2 + d];
+#pragma unroll
+                for (int t = 0; t < NTERM; ++t) o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk][t], B, o, 0, 0, 0);
+              }
+            }
+          }
+          continue;
+        }
         if constexpr (kUe8m0) {
           i32x2 x[2][2][2];  // [buffer][dim block of the quarter][kk]
           auto read_q = [&](int sg, int buf) {
@@ -583,41 +678,50 @@ void decode_ring_kernel(DecodeParams p) {
   if (ep_t >= 0) epilogue(ep_t, ep_s, ep_n);
 }
 
-template <int DQK, int HS, int NB, bool UE>
+template <int DQK, int HS, int NB, int FK>
 static hipError_t launch_ring_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * HS));
   const dim3 block(64 * RingShape<HS>::NW);
   if (precision == 1)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB, UE>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 1, NB, FK>), grid, block, 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB, UE>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 2, NB, FK>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB, UE>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_ring_kernel<DQK, HS, 3, NB, FK>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <int DQK, int HS, int NB>
-static hipError_t launch_ring_any(const DecodeParams& p, int num_parts, int precision, bool ue, hipStream_t stream) {
+static hipError_t launch_ring_any(const DecodeParams& p, int num_parts, int precision, int kind, hipStream_t stream) {
   if constexpr (DQK == 512) {
-    if (ue) return launch_ring_t<DQK, HS, NB, true>(p, num_parts, precision, stream);
+    if (kind == kRingUe8m0) return launch_ring_t<DQK, HS, NB, kRingUe8m0>(p, num_parts, precision, stream);
+    if constexpr (HS > 1) {  // 592-byte ring rows: two buffers of 64 rows leave no room for a second workgroup
+      if (kind == kRingModel1) return launch_ring_t<DQK, HS, NB, kRingModel1>(p, num_parts, precision, stream);
+    }
   }
-  return launch_ring_t<DQK, HS, NB, false>(p, num_parts, precision, stream);
+  return launch_ring_t<DQK, HS, NB, kRingF32Scales>(p, num_parts, precision, stream);
 }
 
 // 16 heads per workgroup: two workgroups per CU, two ring buffers each. 32 heads (eight waves, one
 // workgroup per CU): three ring buffers. 64 heads (eight waves with twice the rows and dims each):
-// three ring buffers, every record gathered once per 64 heads.
+// three ring buffers, every record gathered once per 64 heads. Every list must be of the kind the
+// build takes: FP8_UE8M0 lists only with one another, MODEL1_584 lists likewise and with 32 or more
+// heads per workgroup (launch_decode sends other mixes to the staged kernel).
 hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                               hipStream_t stream) {
-  const bool ue = p.lst[0].format == SDA_FP8_UE8M0;  // then every list is (launch_decode)
+  const int kind = p.lst[0].format == SDA_FP8_UE8M0 ? kRingUe8m0
+                   : p.lst[0].format == SDA_MODEL1_584 ? kRingModel1 : kRingF32Scales;
   if (d_qk == 576) {
-    if (heads_per_group == 16) return launch_ring_any<576, 1, 2>(p, num_parts, precision, false, stream);
-    if (heads_per_group == 32) return launch_ring_any<576, 2, 3>(p, num_parts, precision, false, stream);
-    return launch_ring_any<576, 4, 3>(p, num_parts, precision, false, stream);
+    if (heads_per_group == 16) return launch_ring_any<576, 1, 2>(p, num_parts, precision, kRingF32Scales, stream);
+    if (heads_per_group == 32) return launch_ring_any<576, 2, 3>(p, num_parts, precision, kRingF32Scales, stream);
+    return launch_ring_any<576, 4, 3>(p, num_parts, precision, kRingF32Scales, stream);
   }
-  if (heads_per_group == 16) return launch_ring_any<512, 1, 2>(p, num_parts, precision, ue, stream);
-  if (heads_per_group == 32) return launch_ring_any<512, 2, 3>(p, num_parts, precision, ue, stream);
-  return launch_ring_any<512, 4, 3>(p, num_parts, precision, ue, stream);
+  if (heads_per_group == 16) {
+    if (kind == kRingModel1) return hipErrorInvalidValue;
+    return launch_ring_any<512, 1, 2>(p, num_parts, precision, kind, stream);
+  }
+  if (heads_per_group == 32) return launch_ring_any<512, 2, 3>(p, num_parts, precision, kind, stream);
+  return launch_ring_any<512, 4, 3>(p, num_parts, precision, kind, stream);
 }
 
 }  // namespace sda

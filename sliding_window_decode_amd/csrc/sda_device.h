@@ -136,6 +136,13 @@ __device__ __forceinline__ i32x2 lds_tr8(uint32_t lds_addr) {
   return r;
 }
 
+// ds_read_b64_tr_b16 as inline assembly, for the same reason as lds_tr8 and under the same rule.
+__device__ __forceinline__ i32x2 lds_tr16(uint32_t lds_addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

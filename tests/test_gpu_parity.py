@@ -91,8 +91,9 @@ def test_ue8m0_lists(fmt, xfmt, H, precision):
             count_flips=precision > 1)
 
 
-# MODEL1_584 lists (448 fp8 dims with a power-of-two scale per 64, 64 bf16 dims that are values too) run
-# the staged kernel, alone or with a list of any other 512-dim format
+# MODEL1_584 lists (448 fp8 dims with a power-of-two scale per 64, 64 bf16 dims that are values too): the
+# ring kernel when every list is one and a workgroup takes 32 or more heads (H >= 32 here), else the staged
+# kernel (16 heads, or a list of any other 512-dim format)
 @pytest.mark.parametrize("fmt,xfmt", [(wl.MODEL1_584, wl.MODEL1_584), (wl.MODEL1_584, None),
                                       (wl.MODEL1_584, wl.NVFP4_288), (wl.FP8_528, wl.MODEL1_584),
                                       (wl.FP8_UE8M0, wl.MODEL1_584), (wl.MODEL1_584, wl.FP8_SLOTSCALE)])
@@ -109,16 +110,18 @@ def test_model1_lists(fmt, xfmt, H, precision):
             count_flips=precision > 1)
 
 
-def test_model1_bf16_dims_are_values():
+@pytest.mark.parametrize("H", [16, 32])
+def test_model1_bf16_dims_are_values(H):
     """A single valid MODEL1 row: the output is the row itself, its bf16 dims 448..511 included, exactly;
-    the pad byte changes nothing."""
+    the pad byte changes nothing (16 heads: the staged kernel; 32: the ring kernel, whose gather reads the
+    row's last 16 bytes from record byte 568)."""
     rng = np.random.default_rng(8)
     c = wl.make_cache(rng, wl.MODEL1_584, 64, page_size=16)
-    q = wl.make_q(rng, 3, 16, 512)
+    q = wl.make_q(rng, 3, H, 512)
     idx = np.full((3, 40), -1, dtype=np.int32)
     idx[np.arange(3), [0, 17, 39]] = [5, 16, 63]
     lst = wl.SlotList(idx, 40, np.full(3, 40, dtype=np.int32))
-    w = wl.Workload("model1 rows", 3, 16, 512, 512, q, c, lst, None, None, None, 0.05)
+    w = wl.Workload("model1 rows", 3, H, 512, 512, q, c, lst, None, None, None, 0.05)
     _, out, _ = _run_cmp(w, "model1 rows")
     pages = c.data.reshape(c.num_pages, c.page_stride)
     pages[:, 583::584][:, :16] = 0xFF
@@ -126,14 +129,16 @@ def test_model1_bf16_dims_are_values():
     assert torch.equal(out, out2)
     for t, s in enumerate([5, 16, 63]):
         ref = oracle.decode_slot(c, s)
-        assert np.array_equal(out[t, 0].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
+        for h in (0, H - 1):
+            assert np.array_equal(out[t, h].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
 
 
 # 64-head workgroups (eight waves with 32 rows and 256 dims each) for every fp8 record layout; a call
 # with an NVFP4 list runs 32-head workgroups under the same plan
 @pytest.mark.parametrize("fmt,xfmt,H", [(wl.FP8_SLOTSCALE, None, 64), (wl.FP8_528, wl.FP8_528, 128),
                                         (wl.V32_656, None, 64), (wl.V32_656, None, 128),
-                                        (wl.FP8_528, wl.NVFP4_288, 64), (wl.FP8_UE8M0, wl.FP8_UE8M0, 128)])
+                                        (wl.FP8_528, wl.NVFP4_288, 64), (wl.FP8_UE8M0, wl.FP8_UE8M0, 128),
+                                        (wl.MODEL1_584, wl.MODEL1_584, 128), (wl.MODEL1_584, None, 64)])
 @pytest.mark.parametrize("parts", [5, 40])
 def test_64_head_workgroups(fmt, xfmt, H, parts):
     w = wl.small_workload(70 + fmt + parts, fmt, xfmt, T=7, H=H, width=150, xwidth=260 if xfmt is not None else 0,
