@@ -194,10 +194,14 @@ def whole_tokens_fits(plan: sda_plan, T: int, tiles, v41: bool = False) -> bool:
 
 
 def whole_token_heads_per_group(plan: sda_plan, T: int, H: int, d_qk: int, formats, num_cus: int = 256) -> int:
-    """Heads per workgroup for a whole-token plan: 16 where the call runs the fp8 ring kernel on 512-dim
-    records (no NVFP4 or MODEL1 list) and T x H/16 workgroups fit in one round of two per CU (measured on
-    MI355X: 1.6-3.7 % faster steps than 32-head workgroups, which run one per CU); otherwise the plan's."""
-    ring = all(f not in (NVFP4_288, MODEL1_584) for f in formats if f is not None)
+    """Heads per workgroup for a whole-token plan: 16 where a 16-head call runs the fp8 ring kernel on
+    512-dim records (no NVFP4 or MODEL1 list, FP8_UE8M0 lists only with one another) and T x H/16
+    workgroups fit in one round of two per CU (measured on MI355X: 1.6-3.7 % faster steps than 32-head
+    workgroups, which run one per CU); otherwise the plan's (MODEL1 lists run the ring kernel only with 32
+    or more heads per workgroup, and the staged kernel was slower with 16)."""
+    fmts = [f for f in formats if f is not None]
+    ue = sum(f == FP8_UE8M0 for f in fmts)
+    ring = all(f not in (NVFP4_288, MODEL1_584) for f in fmts) and ue in (0, len(fmts))
     if d_qk == 512 and ring and H % 16 == 0 and plan.heads_per_group == 32 and T * (H // 16) <= 2 * num_cus:
         return 16
     return plan.heads_per_group

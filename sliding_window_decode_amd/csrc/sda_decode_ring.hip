@@ -109,6 +109,7 @@ void decode_ring_kernel(DecodeParams p) {
 
   // list parameters are read from the kernel arguments where used (scalar loads), not held in registers
   auto LD = [&](int L) -> const ListDev& { return p.lst[L]; };
+  touch_args(p);
   int32_t mrec[SDA_META_INTS];
   part_record(p, mrec);
   const int bt = mrec[0], bi = mrec[1], et = mrec[2], ei = mrec[3], bk = mrec[4];

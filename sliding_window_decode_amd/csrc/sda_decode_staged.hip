@@ -1,4 +1,5 @@
-// sda_decode_staged.hip -- split-KV decode attention for calls with an NVFP4 or MODEL1 list, on gfx950: records
+// sda_decode_staged.hip -- split-KV decode attention for calls with an NVFP4 list, with FP8_UE8M0 or MODEL1_584
+// lists mixed with other formats, or with MODEL1_584 lists at 16 heads per workgroup, on gfx950: records
 // staged through registers, widened into a bf16 tile in LDS.
 //
 // Workgroup = one scheduler part x a group of 16 or 32 query heads, 4 waves. Wave w owns output dims

@@ -70,6 +70,16 @@ __device__ __forceinline__ void gen_enter(ItemGen& g, const DecodeParams& p, Src
   if (t + 1 <= g.t_last && t + 1 < p.T) src.issue(p, t + 1);
 }
 
+// Reads one field in each 64-byte line of the kernel arguments, all in one round trip, so that the
+// prologue's later reads of arguments (each issued only behind the branch that needs it) hit the scalar
+// cache instead of missing line after line.
+__device__ __forceinline__ void touch_args(const DecodeParams& p) {
+  static_assert(sizeof(DecodeParams) <= 5 * 64, "one touched field per 64-byte line");
+  const uint64_t a = (uint64_t)p.q ^ (uint64_t)p.l_st ^ (uint64_t)p.lst[0].base ^ (uint64_t)p.lst[1].lens;
+  const uint32_t b = (uint32_t)p.nlists ^ (uint32_t)p.all_partial;
+  asm volatile("" ::"s"(a), "s"(b));
+}
+
 // The part record of this workgroup (the layout gen_init reads): row blockIdx.x of the scheduler's meta
 // array, or, for a whole-token call (no meta array), token blockIdx.x from its first tile to its end,
 // with its clamped lengths read here (one dependent load, in place of the meta record's) and split

@@ -371,5 +371,7 @@ def test_whole_token_heads_per_group():
     assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.MODEL1_584, sda.MODEL1_584]) == 32  # staged kernel
     assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_528, sda.NVFP4_288]) == 32
     assert sda.whole_token_heads_per_group(p32, 512, 32, 512, [sda.FP8_528, None]) == 32  # two rounds
+    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_UE8M0, sda.FP8_UE8M0]) == 16
+    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_UE8M0, sda.FP8_528]) == 32  # staged
     p64 = sda.sda_plan(128, 64, 2, 2, 1)
     assert sda.whole_token_heads_per_group(p64, 128, 128, 576, [sda.V32_656, None]) == 64
