@@ -188,13 +188,21 @@ def main():
 
     import sliding_window_decode_amd as sda
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import DeviceWorkload
+    from gpu_util import DeviceWorkload, auto_plan_for
 
     log(f"[bench] building {args.workload} seed {args.seed}")
     w = wl.make_workload(args.workload, seed=args.seed)
     dw = DeviceWorkload(w)
     X = w.xlst.width if w.xlst is not None else 0
-    plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
+    # the caller's host-side lengths decide between the split schedule and one workgroup per token
+    fmts = [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None]
+    if args.schedule == "auto":
+        plan = auto_plan_for(w)
+    else:
+        plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
+        if args.schedule == "whole":
+            plan.whole_tokens = 1
+            plan.heads_per_group = sda.whole_token_heads_per_group(plan, w.T, w.H, w.d_qk, fmts)
     if args.precision is not None:
         plan.precision = args.precision
     if args.parts is not None:
@@ -203,16 +211,6 @@ def main():
         plan.heads_per_group = args.heads_per_group
     if args.fixed_overhead is not None:
         plan.fixed_overhead = args.fixed_overhead
-    # the caller's host-side lengths decide between the split schedule and one workgroup per token
-    qpl = max(1, getattr(w.lst, "queries_per_len", 1))
-    tiles = sda.token_tiles(w.lst.lens, w.lst.width, w.xlst.lens if w.xlst is not None else None, X, T=w.T,
-                            queries_per_len=qpl)
-    v41 = w.rope is not None
-    if args.schedule == "whole" or (args.schedule == "auto" and sda.whole_tokens_fits(plan, w.T, tiles, v41)):
-        plan.whole_tokens = 1
-        if args.heads_per_group is None:
-            plan.heads_per_group = sda.whole_token_heads_per_group(
-                plan, w.T, w.H, w.d_qk, [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None])
     dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
     out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")

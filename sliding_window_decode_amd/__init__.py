@@ -207,6 +207,20 @@ def whole_token_heads_per_group(plan: sda_plan, T: int, H: int, d_qk: int, forma
     return plan.heads_per_group
 
 
+def auto_plan(T: int, H: int, d_qk: int, width: int, extra_width: int, lens, extra_lens, formats,
+              v41: bool = False, queries_per_len: int = 1) -> sda_plan:
+    """The plan for a call whose lengths the caller holds on the host: sda_make_plan's split plan, turned
+    into a whole-token plan where whole_tokens_fits finds it close enough (heads per workgroup then
+    from whole_token_heads_per_group). formats: the record format of each list (None for no extra
+    list)."""
+    plan = make_plan(T, H, d_qk, width, extra_width)
+    tiles = token_tiles(lens, width, extra_lens, extra_width, T=T, queries_per_len=queries_per_len)
+    if whole_tokens_fits(plan, T, tiles, v41):
+        plan.whole_tokens = 1
+        plan.heads_per_group = whole_token_heads_per_group(plan, T, H, d_qk, formats)
+    return plan
+
+
 def workspace_bytes(T: int, H: int, d_v: int, plan: sda_plan) -> int:
     return int(lib().sda_workspace_bytes(T, H, d_v, ctypes.byref(plan)))
 

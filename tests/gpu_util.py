@@ -5,7 +5,6 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-import oracle
 import sliding_window_decode_amd as sda
 
 # Tolerances: bf16 output vs the round-to-nearest-even bf16 of the fp64 oracle, and fp32 LSE.
@@ -27,6 +26,14 @@ def dev_list(L, device="cuda"):
 
 def dev_q(w, device="cuda"):
     return torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def auto_plan_for(w) -> "sda.sda_plan":
+    """The plan bench.py times for workload w: sda.auto_plan from the workload's host-side lengths."""
+    X = w.xlst.width if w.xlst is not None else 0
+    return sda.auto_plan(w.T, w.H, w.d_qk, w.lst.width, X, w.lst.lens, w.xlst.lens if w.xlst is not None else None,
+                         [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None], w.rope is not None,
+                         max(1, getattr(w.lst, "queries_per_len", 1)))
 
 
 class DeviceWorkload:
@@ -107,19 +114,27 @@ def compare_v41(codes_gpu, scales_gpu, lse_gpu, codes_ref, scales_ref, l_ref, wh
     return info
 
 
+FLIP_RATE = 1e-4  # rounding-boundary flips per element (see compare)
+
+
 def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", count_flips=True):
     """Assert the tolerances; returns a dict of the error figures.
 
     out: every element within 1e-2 of the round-to-nearest-even bf16 of the fp64 oracle, except that an
     element may sit one bf16 ulp away where that ulp itself exceeds 1e-2 (|x| >= 2): a rounding-boundary
     flip, which an fp32 computation produces whenever the exact value lies within its rounding error of
-    a bf16 midpoint. Flips are counted and must stay below 1 in 10^4 elements (count_flips=False lifts
-    that count for the single-term P mode, whose 2^-9 weight rounding flips more of them). rel-L2 <=
-    5e-3 over all elements. lse: within 1e-3 absolute, infinities exact."""
+    a bf16 midpoint. Flips are counted: their number is a random count, so it is held to a rate of 1 in
+    10^4 elements plus a four-sigma Poisson margin (n 1e-4 + 4 sqrt(n 1e-4)); precision 2 measures
+    5e-5 to 9e-5 on the large-magnitude ue8m0 and MODEL1 workloads, where most outputs exceed 2, on
+    both kernels and both schedules (count_flips=False lifts the count for the single-term P mode,
+    whose 2^-9 weight rounding flips more of them). rel-L2 <= 5e-3 over all elements. lse: within 1e-3
+    absolute, infinities exact."""
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     lg = lse_gpu.float().cpu().numpy().astype(np.float64)
     if tokens is not None:
         got, lg = got[tokens], lg[tokens]
+    import oracle  # test infrastructure: imported here, so that bench.py's timed path never loads it
+
     ref = oracle.bf16_rne(o_ref)
     diff = np.abs(got - ref)
     max_abs = float(diff.max()) if diff.size else 0.0
@@ -135,7 +150,9 @@ def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", count_flips=Tr
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert np.all(diff[over] <= ulp[over]), f"{what}: error beyond 1e-2 and beyond one bf16 ulp {info}"
     if count_flips:
-        assert info["ulp_flips"] <= max(1, diff.size // 10000), f"{what}: too many rounding flips {info}"
+        expected = diff.size * FLIP_RATE
+        allowed = max(1, int(expected + 4.0 * np.sqrt(expected)))
+        assert info["ulp_flips"] <= allowed, f"{what}: too many rounding flips (allowed {allowed}) {info}"
     assert rel_l2 <= OUT_REL_L2, f"{what}: out rel-L2 {rel_l2:.3e} {info}"
     assert lse_err <= LSE_MAX_ABS, f"{what}: lse max-abs {lse_err:.3e} {info}"
     return info

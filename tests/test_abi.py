@@ -375,3 +375,24 @@ def test_whole_token_heads_per_group():
     assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_UE8M0, sda.FP8_528]) == 32  # staged
     p64 = sda.sda_plan(128, 64, 2, 2, 1)
     assert sda.whole_token_heads_per_group(p64, 128, 128, 576, [sda.V32_656, None]) == 64
+
+
+def test_auto_plan_choices_on_the_benchmark_workloads():
+    """auto_plan (the plan bench.py times) on the host-side lengths of each workload: whole-token plans
+    except where one long token (C4) or the V4.1 epilogue (c8) favours the split schedule; 16 heads per
+    workgroup only on fp8 ring-kernel calls with 512-dim records."""
+    import workloads as wl
+
+    want = {"c1_tiny_swa": (1, 16), "c2_swa_h128": (1, 16), "c3_swa_fp8extra": (1, 16),
+            "c4_swa_nvfp4extra": (0, None), "c5_topk_v32": (1, 64), "c6_swa_ue8m0": (1, 16),
+            "c7_swa_model1": (1, 32), "c8_v41_ue8m0": (0, None)}
+    for name, (whole, hb) in want.items():
+        w = wl.make_workload(name, seed=0)
+        X = w.xlst.width if w.xlst is not None else 0
+        plan = sda.auto_plan(w.T, w.H, w.d_qk, w.lst.width, X, w.lst.lens,
+                             w.xlst.lens if w.xlst is not None else None,
+                             [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None], w.rope is not None)
+        split = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
+        assert plan.whole_tokens == whole, name
+        assert plan.heads_per_group == (hb if whole else split.heads_per_group), name
+        assert (plan.num_parts, plan.precision) == (split.num_parts, split.precision), name

@@ -15,7 +15,7 @@ import torch
 import oracle
 import sliding_window_decode_amd as sda
 import workloads as wl
-from gpu_util import DeviceWorkload, compare
+from gpu_util import DeviceWorkload, auto_plan_for, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -43,11 +43,13 @@ def test_config_parity_reduced_tokens(name, seed):
 
 @pytest.mark.parametrize("name", wl.CONFIGS)
 def test_config_parity_full_size_sampled(name):
-    """Full-size inputs in the default launch configuration; a sample of tokens checked against the oracle."""
+    """Full-size inputs in the launch configuration bench.py times (auto_plan from the host-side lengths:
+    whole-token plans with their head grouping where chosen, else the split plan); a sample of tokens
+    checked against the oracle."""
     _log(f"[parity-full] {name}")
     w = wl.make_workload(name, seed=0)
     dw = DeviceWorkload(w)
-    out, lse, dec = dw.run()
+    out, lse, dec = dw.run(plan=auto_plan_for(w))
     rng = np.random.default_rng(1)
     toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, size=min(w.T, 6), replace=False)]))
     # the sampled tokens are compared together, so that the rounding-flip allowance (a rate per element)
