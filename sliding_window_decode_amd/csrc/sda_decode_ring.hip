@@ -110,6 +110,22 @@ void decode_ring_kernel(DecodeParams p) {
   // list parameters are read from the kernel arguments where used (scalar loads), not held in registers
   auto LD = [&](int L) -> const ListDev& { return p.lst[L]; };
   touch_args(p);
+  // A whole-token call (no meta array) knows its token before its lengths arrive: the slot ids of list
+  // 0's first NB tiles are loaded first (row min(blockIdx.x, T-1), positions clamped below the width:
+  // always readable), and kept for each of the first items that turns out to be that tile. The lengths
+  // that follow are scalar loads, so waiting for them does not wait for these.
+  const bool spec = p.meta == nullptr;
+  int sid_spec[NB];
+  {
+    const ListDev& l0 = LD(0);
+    const int tb = blockIdx.x < (unsigned)p.T ? (int)blockIdx.x : 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int pos = kTileRows * j + RW * w + lane % RW;
+      sid_spec[j] = l0.idx[(int64_t)tb * l0.row_stride + (pos < l0.width ? pos : l0.width - 1)];
+    }
+  }
+  asm volatile("" ::: "memory");
   int32_t mrec[SDA_META_INTS];
   part_record(p, mrec);
   const int bt = mrec[0], bi = mrec[1], et = mrec[2], ei = mrec[3], bk = mrec[4];
@@ -176,7 +192,12 @@ void decode_ring_kernel(DecodeParams p) {
   {
     int sids[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) sids[j] = load_sid(its[j]);  // every slot id load before any gather
+    for (int j = 0; j < NB; ++j) {  // every slot id load before any gather
+      if (spec && !its[j].end() && its[j].L == 0 && its[j].pos0 == kTileRows * j)
+        sids[j] = kTileRows * j + RW * w + lane % RW < its[j].n ? sid_spec[j] : -1;
+      else
+        sids[j] = load_sid(its[j]);
+    }
 #pragma unroll
     for (int j = 0; j + 1 < NB; ++j) {
       if (!its[j].end()) {

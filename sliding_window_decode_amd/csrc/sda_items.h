@@ -97,8 +97,15 @@ __device__ __forceinline__ void part_record(const DecodeParams& p, int32_t (&m)[
   m[2] = b + 1;
   m[3] = 0;
   m[4] = 0;
-  m[5] = b < p.T ? clamp_len(p.lst[0].lens, p.lst[0].lens_div, p.lst[0].width, b) : 0;
-  m[6] = (b < p.T && p.nlists > 1) ? clamp_len(p.lst[1].lens, p.lst[1].lens_div, p.lst[1].width, b) : 0;
+  // scalar loads (through the constant address space): the caller's lengths are not written while
+  // the kernel runs
+  auto len_of = [&](const ListDev& l) -> int {
+    const int n = l.lens ? *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)(l.lens + b / l.lens_div)
+                         : l.width;
+    return n < 0 ? 0 : (n > l.width ? l.width : n);
+  };
+  m[5] = b < p.T ? len_of(p.lst[0]) : 0;
+  m[6] = (b < p.T && p.nlists > 1) ? len_of(p.lst[1]) : 0;
   m[7] = b;
 }
 
