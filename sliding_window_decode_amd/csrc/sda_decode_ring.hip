@@ -82,9 +82,10 @@ struct RingSmem {
 };
 
 // HS head sets of 16 heads per workgroup (HS = 1, 2, 4: 16, 32 or 64 heads), NB ring buffers (tiles
-// k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'. UE: built for calls whose
-// lists are all FP8_UE8M0 (512 dims), and only for them (carrying both decodings raises the register
-// pressure of every call; calls that mix it with another format run the staged kernel).
+// k+1 .. k+NB-1 in flight while tile k is computed), NTERM bf16 terms of P'. FK (RingKind): the record
+// kind the build decodes; the FP8_UE8M0 and MODEL1_584 builds take calls whose lists are all of that
+// format (512 dims), and only them (carrying several decodings raises the register pressure of every
+// call; calls that mix them with another format run the staged kernel).
 template <int DQK, int HS, int NTERM, int NB, int FK>
 __global__ __launch_bounds__(64 * RingShape<HS>::NW)
 __attribute__((amdgpu_waves_per_eu(RingShape<HS>::NW == 8 || (DQK == 512 && NB == 2) ? 2 : 1)))

@@ -119,7 +119,8 @@ __host__ __device__ inline int64_t part_quantum(int64_t total, int num_parts) {
 
 hipError_t launch_sched(const SchedParams& p, hipStream_t stream);
 // The decode kernels: calls without an NVFP4 list run the ring kernel (sda_decode_ring.hip: records
-// streamed into LDS by global -> LDS loads, fp8 widened as read), the others the staged kernel
+// streamed into LDS by global -> LDS loads, fp8 widened as read), except mixes of FP8_UE8M0 or
+// MODEL1_584 lists with other formats and MODEL1_584 at 16 heads per workgroup; the others the staged kernel
 // (sda_decode_staged.hip: records staged in registers and widened once into a bf16 tile; up to three
 // workgroups per CU hide the cost of the NVFP4 widening and of the gathers better than one with a deep
 // LDS ring); launch_decode (sda_api.cpp) picks one.
