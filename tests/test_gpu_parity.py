@@ -479,6 +479,28 @@ def test_whole_token_plan_16_head_groups(name):
     compare(out, lse, o_ref, l_ref, what=f"{name} whole tokens, 16 heads per group")
 
 
+@pytest.mark.parametrize("fmt,xfmt,width,xwidth,H,hb", [
+    (wl.FP8_SLOTSCALE, wl.FP8_528, 40, 100, 32, 16),   # list 0 narrower than one tile
+    (wl.FP8_528, wl.FP8_528, 200, 70, 32, 32),         # list 0 over four tiles, ragged
+    (wl.MODEL1_584, wl.MODEL1_584, 100, 130, 32, 32),  # MODEL1 on the ring kernel
+    (wl.V32_656, None, 150, 0, 64, 64),                # 576-dim records, 64-head groups
+])
+def test_whole_token_plan_first_tiles(fmt, xfmt, width, xwidth, H, hb):
+    """The first tiles' slot ids of a whole-token workgroup are read before its lengths (and kept only where
+    the first items are list 0's first tiles): narrow and wide main lists, empty main lists (the first
+    items come from the extra list), a row stride past the width, and padded rows."""
+    w = wl.small_workload(600 + width + fmt, fmt, xfmt, T=11, H=H, width=width, xwidth=xwidth, num_slots=2048,
+                          sink=True, p_invalid=0.1, lens_lo=0, row_stride_extra=24)
+    w.lst.lens[[0, 3, 7]] = 0
+    w.lst.lens[[1, 5]] = width
+    plan = _whole_plan(w)
+    plan.heads_per_group = hb
+    _log(f"[whole first tiles] fmt {fmt}/{xfmt} width {width}/{xwidth} H={H} hb={hb}")
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    out, lse, dec = DeviceWorkload(w).run(plan=plan)
+    compare(out, lse, o_ref, l_ref, what=f"whole first tiles {fmt}/{xfmt} {width}/{xwidth}")
+
+
 def test_whole_token_plan_equals_one_token_parts():
     """Where the split schedule gives every part exactly one whole token (64 tokens of two tiles each over 64
     parts at the 128-head SWA shape), the whole-token plan computes the same sums in the same order."""
