@@ -1,13 +1,19 @@
-"""Benchmark of one decode-attention step on one MI355X.
+"""Benchmark of the decode-attention hot path on one MI355X.
 
-A step is the whole hot path on one batch of synthetic, seeded inputs already resident in HBM:
-the device scheduler (sda_get_sched_meta), the split-KV decode kernel and the LSE combine
-(sda_sparse_decode_attn). Default workload: 64 decode tokens x 128 heads, d 512, a 4096-slot paged
-fp8 cache with per-slot scales, window 128, lens U{96..128}.
+A step is the whole op on one batch of synthetic, seeded inputs already resident in HBM: the library's plan
+(sda_choose_plan from the host-side lengths), then the scheduler, the decode kernel and the LSE combine for a
+split plan, or the decode kernel alone for a whole-token plan. The headline (default) workload is the top-k
+configuration: 128 decode tokens x 128 heads, d_qk 576 / d_v 512, 656-byte V3.2 records in a 131072-slot
+paged cache, 2048 slots per token, sink on. It is timed on cold buffers: enough independent copies of q,
+the cache, the slot lists and the outputs are rotated that their total exceeds twice the 256 MB MALL, so
+every call reads from HBM. The timed region is exactly --steps steps between two synchronizations; HIP
+events on the launch stream around each decode-kernel launch inside it give the kernel's mean duration for
+the roofline.
 
-Prints one JSON line with query-tokens/s (value), TFLOP/s and GB/s of algorithmic work, the
-roofline position of the decode kernel (timed alone with HIP events on the same stream) and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line: query-tokens/s (value), the roofline position of the decode kernel and of the whole
+step, per-configuration results for the five benchmark configurations (hot and cold; the top-k one on both
+its whole-token plan and its split-KV + combine plan), and the CPU oracle's throughput on a bounded sample
+of the headline workload (all available host cores, and one thread).
 """
 from __future__ import annotations
 
@@ -16,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -32,6 +39,10 @@ KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
                for f in ("sda_decode_ring.hip", "sda_decode_staged.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
                          "sda_internal.h", "sda_v41.hip")]
 CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
+COLD_BYTES = 600e6             # rotated buffer sets exceed twice the MALL
+HEADLINE = "c5_topk_v32"
+BENCH_CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32")
+BOX_CPU_SHARE = 16             # host CPUs a one-GPU machine allots to a job
 
 
 def log(*a):
@@ -136,21 +147,184 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str):
     print(open(path).read())
 
 
-def cpu_baseline(w, max_seconds: float = 20.0):
+def host_cores() -> int:
+    """Host CPUs this process may use (its affinity set; a one-GPU machine allots BOX_CPU_SHARE of them)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, BOX_CPU_SHARE))
+
+
+def _oracle_rate(w, tokens: int, threads: int, seconds: float):
     import oracle
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    sl = slice(0, tokens)
     t0 = time.perf_counter()
-    oracle.attention(w, nthreads=threads)
-    one = time.perf_counter() - t0
-    passes = max(1, int(10.0 / max(one, 1e-3)))
-    t0 = time.perf_counter()
-    done = 0
-    while done < passes and time.perf_counter() - t0 < max_seconds:
-        oracle.attention(w, nthreads=threads)
+    oracle.attention(w, tokens=sl, nthreads=threads)
+    done, el = 1, time.perf_counter() - t0
+    while el < seconds:
+        oracle.attention(w, tokens=sl, nthreads=threads)
         done += 1
-    el = time.perf_counter() - t0
-    return {"value": done * w.T / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the full workload ({w.T} tokens) {done} times, fp64, {el:.1f} s on {threads} threads"}
+        el = time.perf_counter() - t0
+    return done * tokens / el, done, el
+
+
+def cpu_baseline(w):
+    """The fp64 oracle as it stands on a bounded sample of workload w's tokens: on every available host core,
+    then on one thread (about 10 s and 5 s of CPU work)."""
+    threads = host_cores()
+    n_all = min(w.T, max(1, 2 * threads))
+    v_all, d_all, e_all = _oracle_rate(w, n_all, threads, 10.0)
+    n_one = 1
+    v_one, d_one, e_one = _oracle_rate(w, n_one, 1, 5.0)
+    return {"value": round(v_all, 2), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"tokens 0..{n_all - 1} of {w.T} of the workload, {d_all} passes, fp64, {e_all:.1f} s on "
+                      f"{threads} threads",
+            "single_thread": {"value": round(v_one, 3), "unit": "query-tokens/s", "cores": 1,
+                              "sample": f"token 0, {d_one} passes, {e_one:.1f} s"}}
+
+
+def roofline(byts, flops, t):
+    """Position of a duration t (s) against both roofs; the bound is the roof the algorithmic work hits first."""
+    hbm = byts / t / 1e9
+    tfl = flops / t / 1e12
+    bound = "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if bound == "hbm":
+        r = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm / HBM_PEAK_GBS, 4)}
+    else:
+        r = {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+    r["hbm_frac"] = round(hbm / HBM_PEAK_GBS, 4)
+    r["mfma_frac"] = round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)
+    return r
+
+
+class Runner:
+    """Device inputs and launch plumbing of one workload under one plan: the step is the whole op, with HIP
+    events recorded on the launch stream around its decode-kernel launch."""
+
+    def __init__(self, w, dw, plan):
+        import torch
+
+        import sliding_window_decode_amd as sda
+        self.sda, self.torch = sda, torch
+        self.w, self.dw, self.plan = w, dw, plan
+        self.dec = dw.decoder(plan)
+        self.v41 = getattr(w, "rope", None) is not None
+        dev = dw.q.device
+        self.out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+        if self.v41:
+            self.out8 = torch.empty((w.T, w.H, 512), dtype=torch.uint8, device=dev)
+            self.osc = torch.empty((w.T, w.H, 16), dtype=torch.uint8, device=dev)
+        S = w.T + plan.num_parts
+        off = sda.workspace_lse_offset(w.T, w.H, 512, plan)
+        ws = self.dec.workspace
+        self.o_acc = ws[:S * w.H * 512 * 4].view(torch.float32).view(S, w.H, 512)
+        self.lse_acc = ws[off:off + S * w.H * 4].view(torch.float32).view(S, w.H)
+        self.sets = [(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, self.out, self.lse)]
+
+    def make_cold_sets(self):
+        """Independent copies of q, the caches, the slot lists and the outputs, rotated by the steps so that
+        their total exceeds twice the MALL and each call reads from HBM."""
+        sda, torch, dw = self.sda, self.torch, self.dw
+
+        def cache_copy(c):
+            if c is None:
+                return None
+            return sda.Cache(c.data.clone(), c.num_pages, c.page_size, c.page_stride, c.format,
+                             None if c.slot_scale is None else c.slot_scale.clone())
+
+        def list_copy(L):
+            if L is None:
+                return None
+            return sda.SlotList(L.idx.clone(), L.width, None if L.lens is None else L.lens.clone(), L.queries_per_len)
+
+        per_set = (dw.q.numel() * 2 + self.out.numel() * 2 + dw.cache.data.numel() + dw.lst.idx.numel() * 4 +
+                   (dw.xcache.data.numel() + dw.xlst.idx.numel() * 4 if dw.xcache is not None else 0))
+        nsets = min(64, max(2, int(math.ceil(COLD_BYTES / per_set))))
+        self.sets = [(dw.q.clone(), cache_copy(dw.cache), list_copy(dw.lst), cache_copy(dw.xcache),
+                      list_copy(dw.xlst), torch.empty_like(self.out), torch.empty_like(self.lse))
+                     for _ in range(nsets)]
+        return nsets, per_set
+
+    def step(self, i, ka=None, kb=None):
+        sda, w, plan, dec = self.sda, self.w, self.plan, self.dec
+        q, c, L, xc, xL, out, lse = self.sets[i % len(self.sets)]
+        meta, ns = dec.sched_arrays
+        if self.v41:  # Q RoPE, decode, combine with the inverse RoPE and the MXFP8 cast (one call)
+            dec.schedule(L, xL)
+            if ka is not None:
+                ka.record()
+            sda.sparse_decode_attn_v41(q, c, L, xc, xL, self.dw.sink, w.scale, plan, meta, ns, dec.workspace,
+                                       self.dw.positions, self.dw.cos_sin, self.out8, self.osc, lse)
+            if kb is not None:
+                kb.record()
+            return
+        if plan.whole_tokens:  # one launch: the decode kernel writes every token whole
+            if ka is not None:
+                ka.record()
+            sda.sparse_decode_attn(q, c, L, xc, xL, self.dw.sink, w.scale, plan, None, None, dec.workspace, out, lse)
+            if kb is not None:
+                kb.record()
+            return
+        # split plan: scheduler, decode kernel, combine (the launches sda_sparse_decode_attn makes)
+        dec.schedule(L, xL)
+        if ka is not None:
+            ka.record()
+        sda.decode_splits(q, c, L, xc, xL, self.dw.sink, w.scale, plan, meta, ns, dec.workspace, out, lse)
+        if kb is not None:
+            kb.record()
+        sda.combine_splits(self.o_acc, self.lse_acc, ns, self.dw.sink, out, lse)
+
+    def time(self, steps, warmup):
+        """Mean step (ms) over exactly `steps` steps between two synchronizations, and the decode kernel's mean
+        and median duration (ms) from the events around its launch in each timed step (V4.1: the whole call)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        ka = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        kb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            self.step(i, ka[i], kb[i])
+        e1.record()
+        torch.cuda.synchronize()
+        kern = [a.elapsed_time(b) for a, b in zip(ka, kb)]
+        return e0.elapsed_time(e1) / steps, sum(kern) / steps, statistics.median(kern)
+
+
+def plan_dict(plan):
+    return {"num_parts": plan.num_parts, "heads_per_group": plan.heads_per_group,
+            "fixed_overhead": plan.fixed_overhead, "precision": plan.precision,
+            "whole_tokens": bool(plan.whole_tokens)}
+
+
+def measure(w, dw, plan, steps, warmup, cold=True):
+    """Hot and (optionally) cold timings of one workload under one plan, with rooflines of the whole step
+    and of the decode kernel."""
+    byts, flops, rows = algorithmic_work(w)
+    r = Runner(w, dw, plan)
+    st_h, k_h, km_h = r.time(steps, warmup)
+    res = {"plan": plan_dict(plan), "alg_bytes": byts, "alg_flops": flops, "valid_rows": rows,
+           "hot": {"step_us": round(st_h * 1e3, 2), "kernel_us": round(k_h * 1e3, 2),
+                   "kernel_us_median": round(km_h * 1e3, 2), "query_tokens_per_s": round(w.T / (st_h / 1e3), 1),
+                   "roofline_step": roofline(byts, flops, st_h / 1e3),
+                   "roofline_kernel": roofline(byts, flops, k_h / 1e3)}}
+    if cold:
+        nsets, per_set = r.make_cold_sets()
+        st_c, k_c, km_c = r.time(steps, max(warmup, nsets))
+        res["cold"] = {"step_us": round(st_c * 1e3, 2), "kernel_us": round(k_c * 1e3, 2),
+                       "kernel_us_median": round(km_c * 1e3, 2), "query_tokens_per_s": round(w.T / (st_c / 1e3), 1),
+                       "tflops": round(flops / (st_c / 1e3) / 1e12, 2), "gbps": round(byts / (st_c / 1e3) / 1e9, 1),
+                       "roofline_step": roofline(byts, flops, st_c / 1e3),
+                       "roofline_kernel": roofline(byts, flops, k_c / 1e3),
+                       "buffer_sets": nsets, "set_mb": round(per_set / 1e6, 1)}
+        r.sets = r.sets[:1]
+    return res, r
 
 
 def main():
@@ -158,17 +332,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2_swa_h128", choices=wl.CONFIGS)
+    ap.add_argument("--workload", default=HEADLINE, choices=wl.CONFIGS, help="the headline workload")
+    ap.add_argument("--configs", default=",".join(BENCH_CONFIGS),
+                    help="comma-separated workloads reported per configuration ('none': headline only)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--precision", type=int, default=None, help="override the plan's PV precision (1 or 3)")
+    ap.add_argument("--precision", type=int, default=None, help="override the plan's PV precision (1, 2 or 3)")
     ap.add_argument("--parts", type=int, default=None)
     ap.add_argument("--heads-per-group", type=int, default=None)
     ap.add_argument("--fixed-overhead", type=int, default=None, help="override the plan's per-token tile overhead")
     ap.add_argument("--schedule", choices=["auto", "split", "whole"], default="auto",
-                    help="split: scheduler + combine; whole: one workgroup per token; auto: whole when its "
-                         "makespan in tiles (host-side lengths) is close enough to the split plan's")
+                    help="auto: the library's choice (sda_choose_plan); split: scheduler + combine; whole: one "
+                         "workgroup per token")
+    ap.add_argument("--hot", action="store_true", help="headline on hot buffers (the same buffers every call)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cold", action="store_true", help="also time with rotating buffer sets larger than the MALL")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (calibrates the counter-based traffic)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -187,98 +363,42 @@ def main():
     import torch
 
     import sliding_window_decode_amd as sda
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import DeviceWorkload, auto_plan_for
+    from sliding_window_decode_amd.inputs import DeviceWorkload, plan_for
+
+    def headline_plan(w):
+        plan = plan_for(w)
+        if args.schedule == "split" or (args.schedule == "whole" and not plan.whole_tokens):
+            X = w.xlst.width if w.xlst is not None else 0
+            plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
+            plan.whole_tokens = 1 if args.schedule == "whole" else 0
+        if args.precision is not None:
+            plan.precision = args.precision
+        if args.parts is not None:
+            plan.num_parts = args.parts
+        if args.heads_per_group is not None:
+            plan.heads_per_group = args.heads_per_group
+        if args.fixed_overhead is not None:
+            plan.fixed_overhead = args.fixed_overhead
+        return plan
 
     log(f"[bench] building {args.workload} seed {args.seed}")
     w = wl.make_workload(args.workload, seed=args.seed)
     dw = DeviceWorkload(w)
-    X = w.xlst.width if w.xlst is not None else 0
-    # the caller's host-side lengths decide between the split schedule and one workgroup per token
-    fmts = [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None]
-    if args.schedule == "auto":
-        plan = auto_plan_for(w)
-    else:
-        plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
-        if args.schedule == "whole":
-            plan.whole_tokens = 1
-            plan.heads_per_group = sda.whole_token_heads_per_group(plan, w.T, w.H, w.d_qk, fmts)
-    if args.precision is not None:
-        plan.precision = args.precision
-    if args.parts is not None:
-        plan.num_parts = args.parts
-    if args.heads_per_group is not None:
-        plan.heads_per_group = args.heads_per_group
-    if args.fixed_overhead is not None:
-        plan.fixed_overhead = args.fixed_overhead
-    dec = sda.Decoder(w.T, w.H, w.d_qk, w.lst.width, X, plan=plan)
-    out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    v41 = w.rope is not None
-    if v41:
-        out8 = torch.empty((w.T, w.H, 512), dtype=torch.uint8, device="cuda")
-        osc = torch.empty((w.T, w.H, 16), dtype=torch.uint8, device="cuda")
-
-    meta, num_splits = dec.sched_arrays  # None for a whole-token plan
-
-    def step():
-        dec.schedule(dw.lst, dw.xlst)  # nothing for a whole-token plan
-        if v41:  # Q RoPE, decode, combine with the inverse RoPE and MXFP8 cast
-            sda.sparse_decode_attn_v41(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
-                                       meta, num_splits, dec.workspace, dw.positions, dw.cos_sin, out8, osc, lse)
-        else:
-            sda.sparse_decode_attn(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan,
-                                   meta, num_splits, dec.workspace, out, lse)
-
-    log(f"[bench] plan {plan}; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] step {ms_step * 1e3:.2f} us")
-
-    # the decode kernel alone, back to back on the same stream, launched as in the step (V4.1: every token
-    # leaves as a partial; the rotation of q changes values, not work)
-    def decode_only():
-        sda.decode_splits(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, dw.sink, w.scale, dec.plan, meta,
-                          num_splits, dec.workspace, None if v41 else out, None if v41 else lse)
-
-    for _ in range(max(5, args.warmup // 2)):
-        decode_only()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        decode_only()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_decode = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] decode kernel {ms_decode * 1e3:.2f} us")
-
+    plan = headline_plan(w)
+    log(f"[bench] headline {args.workload}: plan {plan}; {args.steps} steps after {args.warmup} warmup")
     byts, flops, rows = algorithmic_work(w)
-    t_step = ms_step / 1e3
-    t_dec = ms_decode / 1e3
-    gbs_dec = byts / t_dec / 1e9
-    tfl_dec = flops / t_dec / 1e12
-    hbm_frac = gbs_dec / HBM_PEAK_GBS
-    mfma_frac = tfl_dec / MFMA_BF16_PEAK_TFLOPS
-    bound = "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    r = Runner(w, dw, plan)
+    if not args.hot:
+        nsets, per_set = r.make_cold_sets()
+        log(f"[bench] cold: {nsets} buffer sets of {per_set / 1e6:.1f} MB")
+    ms_step, ms_kern, ms_kern_med = r.time(args.steps, max(args.warmup, len(r.sets)))
+    log(f"[bench] step {ms_step * 1e3:.2f} us, decode kernel {ms_kern * 1e3:.2f} us (median {ms_kern_med * 1e3:.2f})")
+    t_step, t_kern = ms_step / 1e3, ms_kern / 1e3
     sha = kernel_sha()
-    traffic = read_traffic(args.workload, sha)
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(gbs_dec, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_frac, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tfl_dec, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(mfma_frac, 4), "traffic": traffic}
-
+    roof = roofline(byts, flops, t_kern)
+    roof_k = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof_k["traffic"] = read_traffic(args.workload, sha)
+    X = w.xlst.width if w.xlst is not None else 0
     result = {
         "metric": "decode-attn query-tokens/s, TFLOP/s and HBM GB/s vs roofline, per head count",
         "value": round(w.T / t_step, 1),
@@ -292,56 +412,44 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": w.T, "heads": w.H, "d_qk": w.d_qk, "d_v": w.d_v,
-                   "list_width": w.lst.width, "extra_width": X,
+        "config": {"workload": args.workload, "buffers": "hot" if args.hot else "cold", "tokens": w.T, "heads": w.H,
+                   "d_qk": w.d_qk, "d_v": w.d_v, "list_width": w.lst.width, "extra_width": X,
                    "format": wl.FORMAT_NAMES[w.cache.fmt],
                    "extra_format": wl.FORMAT_NAMES[w.xcache.fmt] if w.xcache is not None else None,
-                   "sink": w.sink is not None, "valid_rows": rows, "v41_rope_mxfp8_out": v41,
-                   "plan": {"num_parts": plan.num_parts, "heads_per_group": plan.heads_per_group,
-                            "fixed_overhead": plan.fixed_overhead, "precision": plan.precision,
-                            "whole_tokens": bool(plan.whole_tokens)}},
+                   "sink": w.sink is not None, "valid_rows": rows,
+                   "v41_rope_mxfp8_out": getattr(w, "rope", None) is not None, "plan": plan_dict(plan)},
         "tflops": round(flops / t_step / 1e12, 2),
         "gbps": round(byts / t_step / 1e9, 1),
-        "decode_kernel_us": round(ms_decode * 1e3, 2),
-        "roofline": roof,
-        "roofline_both": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
-                          "alg_bytes": byts, "alg_flops": flops},
+        "decode_kernel_us": round(ms_kern * 1e3, 2),
+        "decode_kernel_us_median": round(ms_kern_med * 1e3, 2),
+        "roofline": roof_k,
+        "roofline_step": roofline(byts, flops, t_step),
+        "alg_bytes": byts,
+        "alg_flops": flops,
         "kernel_sha": sha,
     }
+    del r
 
-    if args.cold:
-        # rotate independent copies of q, cache, lists and out so that the working set exceeds the MALL
-        per_set = dw.q.numel() * 2 + out.numel() * 2 + dw.cache.data.numel() + (
-            dw.xcache.data.numel() if dw.xcache is not None else 0)
-        nsets = max(2, int(math.ceil(600e6 / per_set)))
-        nsets = min(nsets, 64)
-        log(f"[bench] cold: {nsets} buffer sets of {per_set / 1e6:.1f} MB")
-        sets = []
-        for _ in range(nsets):
-            c = sda.Cache(dw.cache.data.clone(), dw.cache.num_pages, dw.cache.page_size, dw.cache.page_stride,
-                          dw.cache.format, None if dw.cache.slot_scale is None else dw.cache.slot_scale.clone())
-            xc = None
-            if dw.xcache is not None:
-                xc = sda.Cache(dw.xcache.data.clone(), dw.xcache.num_pages, dw.xcache.page_size,
-                               dw.xcache.page_stride, dw.xcache.format, None)
-            sets.append((dw.q.clone(), c, xc, torch.empty_like(out), torch.empty_like(lse)))
-        for i in range(nsets):
-            q_, c_, xc_, o_, l_ = sets[i]
-            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, meta,
-                                   num_splits, dec.workspace, o_, l_)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            q_, c_, xc_, o_, l_ = sets[i % nsets]
-            dec.schedule(dw.lst, dw.xlst)
-            sda.sparse_decode_attn(q_, c_, dw.lst, xc_, dw.xlst, dw.sink, w.scale, dec.plan, meta,
-                                   num_splits, dec.workspace, o_, l_)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_cold = e0.elapsed_time(e1) / args.steps
-        result["cold"] = {"ms_per_step": round(ms_cold, 5), "value": round(w.T / (ms_cold / 1e3), 1),
-                          "buffer_sets": nsets}
-        del sets
+    configs = [c for c in args.configs.split(",") if c and c != "none"]
+    per = {}
+    for name in configs:
+        log(f"[bench] config {name}")
+        wc = w if (name == args.workload and args.seed == 0) else wl.make_workload(name, seed=0)
+        dwc = dw if wc is w else DeviceWorkload(wc)
+        pc = plan_for(wc)
+        res, _ = measure(wc, dwc, pc, args.steps, args.warmup)
+        entry = {"heads": wc.H, "tokens": wc.T, **res}
+        if name == HEADLINE and pc.whole_tokens:
+            # the plan the configuration names: split-KV sized to 256 CUs + combine
+            sp = sda.make_plan(wc.T, wc.H, wc.d_qk, wc.lst.width, wc.xlst.width if wc.xlst is not None else 0)
+            entry["split_plan"], _ = measure(wc, dwc, sp, args.steps, args.warmup)
+        per[name] = entry
+        log(f"[bench]   {name}: hot {res['hot']['step_us']} us, cold {res['cold']['step_us']} us")
+        if dwc is not dw:
+            del dwc
+        torch.cuda.empty_cache()
+    if per:
+        result["configs"] = per
 
     if args.copy_calib:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")

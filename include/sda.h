@@ -146,6 +146,25 @@ typedef struct sda_plan {
  * <= 0 selects 256). Returns SDA_OK or an error for unsupported shapes. */
 int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cus, sda_plan* plan /*host*/);
 
+/* Host only. The plan for a call whose token lengths the caller holds on the host (a serving engine
+ * keeps them there): sda_make_plan's split plan, or a whole-token plan where the two schedules'
+ * makespans, counted in 64-row tiles from these lengths, say it is faster (the FlashMLA
+ * sparse_decode.h page's get_meta / DecodeImplMeta: the library picks the scheduler parameters).
+ *  format, extra_format   record format of each list (extra_format ignored when extra_width is 0)
+ *  lens, extra_lens       host int32 lengths, one per queries_per_len tokens as in sda_list, or NULL =
+ *                         the width; extra_lens must be NULL when extra_width is 0
+ *  v41                    nonzero for sda_sparse_decode_attn_v41, whose epilogue runs either way
+ * The whole-token plan is taken while its makespan (the longest token, or the even share of the tiles
+ * over num_parts when tokens outnumber parts) is within 1.3x the split plan's (tiles plus
+ * fixed_overhead per token, over num_parts) plus two tiles for the two launches it saves (1.0x plus one
+ * for V4.1); it then takes 16 heads per workgroup instead of 32 on calls whose lists are all 512-dim fp8
+ * records of the fp32-scale or ue8m0 kinds when T x H/16 workgroups fit two per compute unit. Results
+ * do not depend on the choice beyond fp32 summation order. Errors as sda_make_plan, plus unknown
+ * formats or formats whose dims differ from d_qk. */
+int sda_choose_plan(int T, int H, int d_qk, int format, const int32_t* lens /*host, nullable*/, int width,
+                    int extra_format, const int32_t* extra_lens /*host, nullable*/, int extra_width,
+                    int queries_per_len, int v41, int num_cus, sda_plan* plan /*host*/);
+
 /* Host only. Bytes of workspace sda_sparse_decode_attn needs for this plan: the fp32 split partials
  * o_accum [T + num_parts][H][d_v] and lse_accum [T + num_parts][H] (FlashMLA sparse_decode.h:
  * total_num_splits = b + num_sm_parts), plus room for the meta arrays when the caller passes none. */
@@ -270,7 +289,8 @@ size_t sda_workspace_lse_offset(int T, int H, int d_v, const sda_plan* plan /*ho
  *   M = max(sink_h, lse_accum[s][h]), den = exp(sink_h - M) + sum_k exp(lse_accum[s][h] - M),
  *   out = sum_k exp(lse_accum[s][h] - M) * o_accum[s][h][:] / den,  lse = M + ln(den).
  * o_accum [*][H][d_v] fp32 holds normalized partials; a part with no rows has lse -inf. Tokens with
- * n_t < 2 are left untouched (the decode kernel writes them directly). */
+ * n_t < 2 are left untouched (the decode kernel writes them directly). H in {16, 32, 64, 128}, d_v = 512;
+ * o_accum and out 16-byte aligned, out strides multiples of 8 elements. */
 int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float* lse_accum,
                        const int32_t* num_splits, const float* attn_sink, void* out, int64_t out_stride_t,
                        int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream);

@@ -20,7 +20,7 @@ META_INTS = 8
 
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTED_SYMBOLS = ("sda_make_plan", "sda_workspace_bytes", "sda_get_sched_meta", "sda_get_sched_meta_host",
+EXPORTED_SYMBOLS = ("sda_make_plan", "sda_choose_plan", "sda_workspace_bytes", "sda_get_sched_meta", "sda_get_sched_meta_host",
                     "sda_sparse_decode_attn", "sda_decode_splits", "sda_workspace_lse_offset",
                     "sda_combine_splits", "sda_status_string", "sda_last_error", "sda_record_bytes",
                     "sda_format_dims", "sda_workspace_bytes_v41", "sda_sparse_decode_attn_v41")
@@ -73,6 +73,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.sda_make_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sda_plan)]
+        L.sda_choose_plan.argtypes = [i32, i32, i32, i32, vp, i32, i32, vp, i32, i32, i32, i32,
+                                      ctypes.POINTER(sda_plan)]
         L.sda_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sda_plan)]
         L.sda_workspace_bytes.restype = sz
         L.sda_get_sched_meta.argtypes = [i32, ctypes.POINTER(sda_list), ctypes.POINTER(sda_list),
@@ -151,73 +153,19 @@ def make_plan(T: int, H: int, d_qk: int, width: int, extra_width: int = 0, num_c
     return plan
 
 
-def token_tiles(lens, width: int, extra_lens=None, extra_width: int = 0, T: Optional[int] = None,
-                queries_per_len: int = 1):
-    """Host-side 64-row tile count of every token (numpy int array of length T): ceil(n / 64) per list with
-    n the length clamped to [0, width] (the width when lens is None), at least one tile per token. lens
-    holds one entry per queries_per_len consecutive tokens."""
-    import numpy as np
-
-    def per_list(ls, w):
-        if w <= 0:
-            return 0
-        if ls is None:
-            return np.full(T, (w + 63) // 64, dtype=np.int64)
-        n = np.clip(np.asarray(ls, dtype=np.int64), 0, w)
-        n = np.repeat(n, max(1, queries_per_len))[:T] if queries_per_len > 1 else n[:T]
-        return (n + 63) // 64
-
-    if T is None:
-        T = len(lens) * max(1, queries_per_len)
-    return np.maximum(per_list(lens, width) + per_list(extra_lens, extra_width), 1)
-
-
-def whole_tokens_fits(plan: sda_plan, T: int, tiles, v41: bool = False) -> bool:
-    """Caller policy for a whole-token plan, from host-side tile counts (token_tiles): compares the
-    makespans of the two schedules in 64-row tiles. One workgroup per token takes about the longest
-    token (or the even share sum / num_parts once tokens outnumber the split plan's parts); the split
-    plan takes about (sum + T x fixed overhead) / num_parts and two more launches (scheduler
-    and combine; only the scheduler for the V4.1 call, which still merges in its epilogue), each worth
-    about a tile. The whole-token plan is chosen while its makespan is within 1.3x the split one plus
-    two tiles (1.0x plus one for V4.1): measured on MI355X, it wins where tokens are equal or a few
-    tiles apart (the split plan also pays its partial writes and token switches) and loses where one
-    long token leaves the GPU idle. Results do not depend on the choice."""
-    import numpy as np
-    tiles = np.asarray(tiles, dtype=np.int64)
-    if tiles.size != T or T < 1:
-        return False
-    total = int(tiles.sum())
-    whole = max(int(tiles.max()), -(-total // plan.num_parts))
-    split = (total + T * plan.fixed_overhead) / plan.num_parts
-    ratio, slack = (1.0, 1.0) if v41 else (1.3, 2.0)
-    return whole <= ratio * split + slack
-
-
-def whole_token_heads_per_group(plan: sda_plan, T: int, H: int, d_qk: int, formats, num_cus: int = 256) -> int:
-    """Heads per workgroup for a whole-token plan: 16 where a 16-head call runs the fp8 ring kernel on
-    512-dim records (no NVFP4 or MODEL1 list, FP8_UE8M0 lists only with one another) and T x H/16
-    workgroups fit in one round of two per CU (measured on MI355X: 1.6-3.7 % faster steps than 32-head
-    workgroups, which run one per CU); otherwise the plan's (MODEL1 lists run the ring kernel only with 32
-    or more heads per workgroup, and the staged kernel was slower with 16)."""
-    fmts = [f for f in formats if f is not None]
-    ue = sum(f == FP8_UE8M0 for f in fmts)
-    ring = all(f not in (NVFP4_288, MODEL1_584) for f in fmts) and ue in (0, len(fmts))
-    if d_qk == 512 and ring and H % 16 == 0 and plan.heads_per_group == 32 and T * (H // 16) <= 2 * num_cus:
-        return 16
-    return plan.heads_per_group
-
-
 def auto_plan(T: int, H: int, d_qk: int, width: int, extra_width: int, lens, extra_lens, formats,
-              v41: bool = False, queries_per_len: int = 1) -> sda_plan:
-    """The plan for a call whose lengths the caller holds on the host: sda_make_plan's split plan, turned
-    into a whole-token plan where whole_tokens_fits finds it close enough (heads per workgroup then
-    from whole_token_heads_per_group). formats: the record format of each list (None for no extra
-    list)."""
-    plan = make_plan(T, H, d_qk, width, extra_width)
-    tiles = token_tiles(lens, width, extra_lens, extra_width, T=T, queries_per_len=queries_per_len)
-    if whole_tokens_fits(plan, T, tiles, v41):
-        plan.whole_tokens = 1
-        plan.heads_per_group = whole_token_heads_per_group(plan, T, H, d_qk, formats)
+              v41: bool = False, queries_per_len: int = 1, num_cus: int = 256) -> sda_plan:
+    """sda_choose_plan: the library's plan for a call whose lengths the caller holds on the host (numpy int32
+    arrays, one entry per queries_per_len tokens, or None = the width). formats: the record format of each
+    list (None for no extra list)."""
+    import numpy as np
+    plan = sda_plan()
+    l0 = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
+    l1 = None if extra_lens is None or extra_width <= 0 else np.ascontiguousarray(extra_lens, dtype=np.int32)
+    xf = formats[1] if len(formats) > 1 and formats[1] is not None else -1
+    _check(lib().sda_choose_plan(T, H, d_qk, formats[0], None if l0 is None else l0.ctypes.data, width, xf,
+                                 None if l1 is None else l1.ctypes.data, extra_width if xf >= 0 else 0,
+                                 queries_per_len, 1 if v41 else 0, num_cus, ctypes.byref(plan)))
     return plan
 
 

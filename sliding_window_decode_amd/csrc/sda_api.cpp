@@ -249,6 +249,61 @@ int sda_make_plan(int T, int H, int d_qk, int width, int extra_width, int num_cu
   return SDA_OK;
 }
 
+// The choice between the split plan and a whole-token plan compares the two schedules' makespans in
+// 64-row tiles. One workgroup per token takes about the longest token's tiles, or the even share
+// total / num_parts once tokens outnumber the split plan's parts; the split plan takes about
+// (total + T x fixed overhead) / num_parts and two more launches (scheduler and combine; the V4.1 call
+// keeps its epilogue, so it saves only the scheduler), each worth about a tile. The whole-token plan is
+// taken while its makespan is within 1.3x the split one plus two tiles (1.0x plus one for V4.1):
+// measured on MI355X, it wins where tokens are equal or a few tiles apart (the split plan also pays its
+// partial writes and token switches) and loses where one long token leaves the GPU idle.
+int sda_choose_plan(int T, int H, int d_qk, int format, const int32_t* lens, int width, int extra_format,
+                    const int32_t* extra_lens, int extra_width, int queries_per_len, int v41, int num_cus,
+                    sda_plan* plan) {
+  if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
+  if (queries_per_len < 0) return fail(SDA_ERR_INVALID_ARG, "queries_per_len must be >= 0");
+  if (sda_record_bytes(format) < 0 || sda_format_dims(format) != d_qk)
+    return fail(SDA_ERR_UNSUPPORTED, "main list format unknown or not of d_qk dims");
+  const bool has_extra = extra_width > 0;
+  if (has_extra && (sda_record_bytes(extra_format) < 0 || sda_format_dims(extra_format) != d_qk))
+    return fail(SDA_ERR_UNSUPPORTED, "extra list format unknown or not of d_qk dims");
+  if (!has_extra && extra_lens) return fail(SDA_ERR_INVALID_ARG, "extra_lens without an extra list");
+  int rc = sda_make_plan(T, H, d_qk, width, has_extra ? extra_width : 0, num_cus, plan);
+  if (rc) return rc;
+  if (num_cus <= 0) num_cus = 256;
+  const int div = queries_per_len > 1 ? queries_per_len : 1;
+  int64_t total = 0, longest = 0;
+  for (int t = 0; t < T; ++t) {
+    const int n0 = sda::clamp_len(lens, div, width, t);
+    const int n1 = has_extra ? sda::clamp_len(extra_lens, div, extra_width, t) : 0;
+    const int64_t nt = sda::token_tiles(n0, n1);
+    total += nt;
+    if (nt > longest) longest = nt;
+  }
+  const int64_t share = (total + plan->num_parts - 1) / plan->num_parts;
+  const double whole = (double)(longest > share ? longest : share);
+  const double split = (double)(total + (int64_t)T * plan->fixed_overhead) / plan->num_parts;
+  const double ratio = v41 ? 1.0 : 1.3, slack = v41 ? 1.0 : 2.0;
+  if (!(whole <= ratio * split + slack)) return SDA_OK;
+  plan->whole_tokens = 1;
+  // 16 heads per workgroup where the call runs the fp8 ring kernel on 512-dim records (no NVFP4 or MODEL1
+  // list; FP8_UE8M0 lists only with one another) and T x H/16 workgroups fit one round of two per CU: the
+  // four-wave workgroups overlap one another's gathers (measured 1.6-3.7 % faster steps than 32-head
+  // workgroups). MODEL1 lists run the ring kernel only with 32 or more heads per workgroup.
+  const int fm[2] = {format, has_extra ? extra_format : -1};
+  const int nf = has_extra ? 2 : 1;
+  int ue = 0;
+  bool ring = true;
+  for (int i = 0; i < nf; ++i) {
+    ue += fm[i] == SDA_FP8_UE8M0;
+    if (fm[i] == SDA_NVFP4_288 || fm[i] == SDA_MODEL1_584) ring = false;
+  }
+  if (ue != 0 && ue != nf) ring = false;
+  if (d_qk == 512 && ring && plan->heads_per_group == 32 && (int64_t)T * (H / 16) <= 2 * (int64_t)num_cus)
+    plan->heads_per_group = 16;
+  return SDA_OK;
+}
+
 size_t sda_workspace_bytes(int T, int H, int d_v, const sda_plan* plan) {
   if (!plan || T < 1 || H < 1 || d_v < 1 || plan->num_parts < 1) return 0;
   return layout_of(T, H, d_v, plan->num_parts).total;
@@ -504,11 +559,15 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
 int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float* lse_accum, const int32_t* num_splits,
                        const float* attn_sink, void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
                        int64_t lse_stride_t, void* stream) {
-  if (T < 1 || H < 1) return fail(SDA_ERR_INVALID_ARG, "T and H must be >= 1");
+  if (T < 1) return fail(SDA_ERR_INVALID_ARG, "T must be >= 1");
+  // the combine kernel computes 16 heads per workgroup (one wave each) and stores 8 bf16 per lane
+  if (!supported_heads(H)) return fail(SDA_ERR_UNSUPPORTED, "H must be 16, 32, 64 or 128");
   if (d_v != 512) return fail(SDA_ERR_UNSUPPORTED, "d_v must be 512");
   if (!o_accum || !lse_accum || !num_splits || !out || !lse) return fail(SDA_ERR_INVALID_ARG, "NULL buffer");
-  if (!aligned(o_accum, 16) || !aligned(out, 8) || out_stride_h % 4 || out_stride_t % 4 || out_stride_h < d_v)
-    return fail(SDA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, out 8-byte aligned with strides in 4s");
+  if (!aligned(o_accum, 16) || !aligned(out, 16) || out_stride_h % 8 || out_stride_t % 8 || out_stride_h < d_v ||
+      out_stride_t < 0)
+    return fail(SDA_ERR_INVALID_ARG,
+                "o_accum and out must be 16-byte aligned, out strides multiples of 8 elements");
   if (lse_stride_t < H) return fail(SDA_ERR_INVALID_ARG, "lse_stride_t must be >= H");
   const sda::CombineParams c = combine_params(T, H, o_accum, lse_accum, num_splits, attn_sink, out, out_stride_t,
                                              out_stride_h, lse, lse_stride_t);

@@ -162,6 +162,17 @@ def test_combine_rejects_bad_arguments():
                                 None) == sda.SDA_ERR_UNSUPPORTED
     assert L.sda_combine_splits(2, 16, 512, None, 1 << 21, 1 << 22, None, 1 << 23, 8192, 512, 1 << 24, 16,
                                 None) == sda.SDA_ERR_INVALID_ARG
+    # head counts the kernel's 16-head workgroups do not cover exactly
+    for H in (1, 8, 17, 24, 48, 256):
+        assert L.sda_combine_splits(2, H, 512, 1 << 20, 1 << 21, 1 << 22, None, 1 << 23, 8192, 512, 1 << 24, 256,
+                                    None) == sda.SDA_ERR_UNSUPPORTED, H
+    # out must be 16-byte aligned with strides in multiples of 8 elements (the kernel stores 8 bf16 per lane)
+    for out, st, sh in [((1 << 23) + 8, 8192, 512), (1 << 23, 8196, 512), (1 << 23, 8192, 516),
+                        (1 << 23, -8, 512), (1 << 23, 8192, 504)]:
+        assert L.sda_combine_splits(2, 16, 512, 1 << 20, 1 << 21, 1 << 22, None, out, st, sh, 1 << 24, 16,
+                                    None) == sda.SDA_ERR_INVALID_ARG, (out, st, sh)
+    assert L.sda_combine_splits(2, 16, 512, (1 << 20) + 8, 1 << 21, 1 << 22, None, 1 << 23, 8192, 512, 1 << 24, 16,
+                                None) == sda.SDA_ERR_INVALID_ARG
 
 
 # ------------------------------------------------------------------ host scheduler
@@ -339,49 +350,79 @@ def test_whole_token_plans_on_the_host():
     assert sda.make_plan(64, 128, 512, 128).whole_tokens == 0
 
 
-def test_whole_token_policy_helpers():
-    """token_tiles counts ceil(n / 64) per list (clamped lengths, widths when absent, at least one tile, lengths
-    per request repeated over their queries); whole_tokens_fits compares the two schedules' makespans."""
-    tiles = sda.token_tiles(np.array([0, 1, 64, 65, 200, -3], np.int32), 128, None, 512)
-    assert list(tiles) == [8, 9, 9, 10, 10, 8]
-    assert list(sda.token_tiles(None, 2048, T=3)) == [32, 32, 32]
-    assert list(sda.token_tiles(np.array([0, 0], np.int32), 128)) == [1, 1]
-    assert list(sda.token_tiles(np.array([70, 10], np.int32), 128, T=5, queries_per_len=3)) == [2, 2, 2, 1, 1]
-    # equal tokens, one per part: whole
-    assert sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 64, np.full(64, 2))
-    # a handful of tokens on a GPU-wide split plan: the two launches outweigh one extra tile
-    assert sda.whole_tokens_fits(sda.sda_plan(768, 16, 0, 2), 4, np.array([2, 1, 2, 2]))
-    # tokens a few tiles apart (2..10, as the SWA + extra-list shape): whole for the plain call, split for V4.1
-    t = np.r_[np.full(128, 10), np.full(128, 2)]
-    assert sda.whole_tokens_fits(sda.sda_plan(256, 32, 2, 2), 256, t)
-    assert not sda.whole_tokens_fits(sda.sda_plan(256, 32, 2, 2), 256, t, v41=True)
-    # one long token per workgroup against balanced parts (2..34 tiles over 768 parts): split
-    t = np.r_[np.full(256, 34), np.full(256, 2)]
-    assert not sda.whole_tokens_fits(sda.sda_plan(768, 16, 0, 2), 512, t)
-    # more tokens than parts: the even share bounds the whole-token makespan
-    assert sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 640, np.full(640, 2))
-    assert not sda.whole_tokens_fits(sda.sda_plan(64, 32, 2, 2), 63, np.full(64, 2))
+def _choose(T, H, d_qk, fmt, lens, width, xfmt=None, xlens=None, xwidth=0, v41=False, qpl=1):
+    return sda.auto_plan(T, H, d_qk, width, xwidth if xfmt is not None else 0, lens, xlens, [fmt, xfmt], v41, qpl)
 
 
-def test_whole_token_heads_per_group():
-    """16-head workgroups for whole-token calls on the fp8 ring kernel when they fit one round of two per CU."""
-    p32 = sda.sda_plan(64, 32, 2, 2, 1)
-    assert sda.whole_token_heads_per_group(p32, 64, 128, 512, [sda.FP8_SLOTSCALE, None]) == 16
-    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_528, sda.FP8_528]) == 16
-    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.MODEL1_584, sda.MODEL1_584]) == 32  # staged kernel
-    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_528, sda.NVFP4_288]) == 32
-    assert sda.whole_token_heads_per_group(p32, 512, 32, 512, [sda.FP8_528, None]) == 32  # two rounds
-    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_UE8M0, sda.FP8_UE8M0]) == 16
-    assert sda.whole_token_heads_per_group(p32, 256, 32, 512, [sda.FP8_UE8M0, sda.FP8_528]) == 32  # staged
-    p64 = sda.sda_plan(128, 64, 2, 2, 1)
-    assert sda.whole_token_heads_per_group(p64, 128, 128, 576, [sda.V32_656, None]) == 64
+def test_choose_plan_makespan_rule():
+    """sda_choose_plan: whole-token plan while its makespan in tiles (longest token, or the even share once
+    tokens outnumber parts) is within 1.3x the split plan's plus two (1.0x plus one for V4.1)."""
+    F8, F528 = sda.FP8_SLOTSCALE, sda.FP8_528
+    # equal tokens, one per part (64 tokens of 2 tiles, 64 parts): whole, 16-head workgroups in one round
+    p = _choose(64, 128, 512, F8, np.full(64, 100, np.int32), 128)
+    assert (p.whole_tokens, p.heads_per_group, p.num_parts) == (1, 16, 64)
+    # a handful of tokens on a GPU-wide split plan (768 parts of 16 heads): the two launches outweigh a tile
+    p = _choose(4, 16, 512, F528, np.array([100, 50, 128, 90], np.int32), 128)
+    assert (p.num_parts, p.fixed_overhead, p.whole_tokens, p.heads_per_group) == (768, 0, 1, 16)
+    # tokens 2 and 10 tiles long (SWA + extra list shape): whole for the plain call, split for V4.1
+    lens = np.r_[np.full(128, 128), np.full(128, 64)].astype(np.int32)
+    xlens = np.r_[np.full(128, 512), np.full(128, 64)].astype(np.int32)
+    p = _choose(256, 32, 512, F528, lens, 128, F528, xlens, 512)
+    assert (p.num_parts, p.whole_tokens, p.heads_per_group) == (256, 1, 16)
+    p = _choose(256, 32, 512, sda.FP8_UE8M0, lens, 128, sda.FP8_UE8M0, xlens, 512, v41=True)
+    assert p.whole_tokens == 0 and p.heads_per_group == 32
+    # one long token per workgroup against balanced parts (2 and 34 tiles over 768 parts): split
+    lens = np.r_[np.full(256, 128), np.full(256, 64)].astype(np.int32)
+    xlens = np.r_[np.full(256, 2048), np.full(256, 64)].astype(np.int32)
+    p = _choose(512, 16, 512, F528, lens, 128, sda.NVFP4_288, xlens, 2048)
+    assert (p.num_parts, p.whole_tokens) == (768, 0)
+    # more tokens than parts: the even share bounds the whole-token makespan; two rounds keep 32 heads
+    p = _choose(640, 128, 512, F8, None, 128)
+    assert (p.num_parts, p.whole_tokens, p.heads_per_group) == (64, 1, 32)
+    # lengths per request repeated over their queries: the same choice as the expanded lengths
+    g = _choose(12, 32, 512, F528, np.array([128, 0, 64, 128], np.int32), 128, qpl=3)
+    e = _choose(12, 32, 512, F528, np.repeat(np.array([128, 0, 64, 128], np.int32), 3), 128)
+    assert (g.whole_tokens, g.heads_per_group, g.num_parts) == (e.whole_tokens, e.heads_per_group, e.num_parts)
 
 
-def test_auto_plan_choices_on_the_benchmark_workloads():
-    """auto_plan (the plan bench.py times) on the host-side lengths of each workload: whole-token plans
-    except where one long token (C4) or the V4.1 epilogue (c8) favours the split schedule; 16 heads per
-    workgroup only on fp8 ring-kernel calls with 512-dim records."""
+def test_choose_plan_head_grouping():
+    """16 heads per workgroup only for whole-token calls on the fp8 ring kernel with 512-dim records (no NVFP4 or
+    MODEL1 list, ue8m0 lists only with one another) whose T x H/16 workgroups fit two per CU."""
+    L = np.full(256, 128, np.int32)
+    F528, UE, M1, F4 = sda.FP8_528, sda.FP8_UE8M0, sda.MODEL1_584, sda.NVFP4_288
+    assert _choose(256, 32, 512, F528, L, 128, F528, L, 128).heads_per_group == 16
+    assert _choose(256, 32, 512, UE, L, 128, UE, L, 128).heads_per_group == 16
+    assert _choose(256, 32, 512, UE, L, 128, F528, L, 128).heads_per_group == 32   # staged kernel
+    assert _choose(256, 32, 512, M1, L, 128, M1, L, 128).heads_per_group == 32     # 592-byte ring rows
+    assert _choose(256, 32, 512, F528, L, 128, F4, L, 128).heads_per_group == 32   # staged kernel
+    p = _choose(128, 128, 576, sda.V32_656, None, 2048)
+    assert (p.whole_tokens, p.heads_per_group) == (1, 64)
+
+
+def test_choose_plan_rejects_bad_arguments():
+    for kw, status in [(dict(fmt=9), sda.SDA_ERR_UNSUPPORTED), (dict(fmt=sda.V32_656), sda.SDA_ERR_UNSUPPORTED),
+                       (dict(xfmt=sda.V32_656, xwidth=64), sda.SDA_ERR_UNSUPPORTED),
+                       (dict(H=24), sda.SDA_ERR_UNSUPPORTED), (dict(T=0), sda.SDA_ERR_INVALID_ARG),
+                       (dict(qpl=-1), sda.SDA_ERR_INVALID_ARG)]:
+        args = dict(T=4, H=16, d_qk=512, fmt=sda.FP8_528, lens=None, width=64)
+        args.update(kw)
+        with pytest.raises(sda.SdaError) as ei:
+            _choose(**args)
+        assert ei.value.status == status, kw
+    # extra lengths without an extra list
+    plan = sda.sda_plan()
+    L = np.full(4, 10, np.int32)
+    rc = sda.lib().sda_choose_plan(4, 16, 512, sda.FP8_528, None, 64, sda.FP8_528, L.ctypes.data, 0, 1, 0, 256,
+                                   ctypes.byref(plan))
+    assert rc == sda.SDA_ERR_INVALID_ARG
+
+
+def test_choose_plan_on_the_benchmark_workloads():
+    """The plan bench.py times, on the host-side lengths of each workload: whole-token plans except where one
+    long token (C4) or the V4.1 epilogue (c8) favours the split schedule; 16 heads per workgroup only on fp8
+    ring-kernel calls with 512-dim records."""
     import workloads as wl
+    from sliding_window_decode_amd.inputs import plan_for
 
     want = {"c1_tiny_swa": (1, 16), "c2_swa_h128": (1, 16), "c3_swa_fp8extra": (1, 16),
             "c4_swa_nvfp4extra": (0, None), "c5_topk_v32": (1, 64), "c6_swa_ue8m0": (1, 16),
@@ -389,9 +430,7 @@ def test_auto_plan_choices_on_the_benchmark_workloads():
     for name, (whole, hb) in want.items():
         w = wl.make_workload(name, seed=0)
         X = w.xlst.width if w.xlst is not None else 0
-        plan = sda.auto_plan(w.T, w.H, w.d_qk, w.lst.width, X, w.lst.lens,
-                             w.xlst.lens if w.xlst is not None else None,
-                             [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None], w.rope is not None)
+        plan = plan_for(w)
         split = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
         assert plan.whole_tokens == whole, name
         assert plan.heads_per_group == (hb if whole else split.heads_per_group), name

@@ -1,10 +1,10 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle on an MI355X.
 
-Bar (tests/gpu_util.compare): bf16 output within max-abs 1e-2 of the RNE-bf16 oracle, up to counted
-one-ulp rounding-boundary flips where one ulp exceeds 1e-2; rel-L2 5e-3; LSE within 1e-3 absolute
-(infinities exact). Sizes span several 64-row tiles and ragged tails; the five configurations run at
-reduced token counts with the full oracle, and at full size in the benchmark's launch configuration
-on sampled tokens."""
+Bar (tests/gpu_util.compare): every bf16 output element within max-abs 1e-2 of the RNE-bf16 oracle, or a
+correct bf16 rounding of a value within the kernel's fp32 error budget of the oracle's (where that value
+sits at a rounding midpoint and one ulp exceeds 1e-2); rel-L2 5e-3; LSE within 1e-3 absolute
+(infinities exact). Sizes span several 64-row tiles and ragged tails; the configurations run at reduced
+token counts with three seeds, and at full size, every token, in the benchmark's launch configuration."""
 import copy
 import sys
 
@@ -15,7 +15,7 @@ import torch
 import oracle
 import sliding_window_decode_amd as sda
 import workloads as wl
-from gpu_util import DeviceWorkload, auto_plan_for, compare
+from gpu_util import EPS_FP32, EPS_P1, DeviceWorkload, auto_plan_for, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -41,27 +41,27 @@ def test_config_parity_reduced_tokens(name, seed):
     _log(f"  {dec.plan} {info}")
 
 
-@pytest.mark.parametrize("name", wl.CONFIGS)
-def test_config_parity_full_size_sampled(name):
-    """Full-size inputs in the launch configuration bench.py times (auto_plan from the host-side lengths:
-    whole-token plans with their head grouping where chosen, else the split plan); a sample of tokens
-    checked against the oracle."""
-    _log(f"[parity-full] {name}")
+def _full_size_cases():
+    cases = [(n, "auto") for n in wl.CONFIGS]
+    # the top-k configuration also on the plan its description names: split-KV sized to 256 CUs + combine
+    cases.append(("c5_topk_v32", "split"))
+    return cases
+
+
+@pytest.mark.parametrize("name,schedule", _full_size_cases())
+def test_config_parity_full_size(name, schedule):
+    """Full-size inputs, every token against the oracle: in the launch configuration bench.py times
+    (sda_choose_plan from the host-side lengths), and for the top-k configuration also on the split plan."""
     w = wl.make_workload(name, seed=0)
+    plan = auto_plan_for(w)
+    if schedule == "split":
+        plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0)
+    _log(f"[parity-full] {name} T={w.T} {plan}")
     dw = DeviceWorkload(w)
-    out, lse, dec = dw.run(plan=auto_plan_for(w))
-    rng = np.random.default_rng(1)
-    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, size=min(w.T, 6), replace=False)]))
-    # the sampled tokens are compared together, so that the rounding-flip allowance (a rate per element)
-    # is applied to all of them rather than rounded down to one flip per token
-    refs = [oracle.attention(w, tokens=slice(int(t), int(t) + 1), nthreads=8) for t in toks]
-    o_ref = np.concatenate([r[0] for r in refs])
-    l_ref = np.concatenate([r[1] for r in refs])
-    ti = torch.as_tensor(toks, device=out.device)
-    compare(out[ti], lse[ti], o_ref, l_ref, what=f"{name} tokens {list(toks)}")
-    # properties that hold at any size: finite outputs, LSE >= max over sink, outputs bounded by rows
-    assert torch.isfinite(out.float()).all()
-    _log(f"  {dec.plan} checked tokens {list(toks)}")
+    out, lse, dec = dw.run(plan=plan)
+    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    info = compare(out, lse, o_ref, l_ref, what=f"{name} full size, {schedule} plan")
+    _log(f"  {info}")
 
 
 # ------------------------------------------------------------------ plans: results independent of the split
@@ -90,7 +90,7 @@ def test_ue8m0_lists(fmt, xfmt, H, precision):
     plan.precision = precision
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
     compare(out, lse, o_ref, l_ref, what=f"ue8m0 {fmt}/{xfmt} H={H} precision {precision}",
-            count_flips=precision > 1)
+            eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
 # MODEL1_584 lists (448 fp8 dims with a power-of-two scale per 64, 64 bf16 dims that are values too): the
@@ -109,7 +109,7 @@ def test_model1_lists(fmt, xfmt, H, precision):
     plan.precision = precision
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
     compare(out, lse, o_ref, l_ref, what=f"model1 {fmt}/{xfmt} H={H} precision {precision}",
-            count_flips=precision > 1)
+            eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
 @pytest.mark.parametrize("H", [16, 32])
@@ -148,7 +148,7 @@ def test_64_head_workgroups(fmt, xfmt, H, parts):
     o_ref, l_ref = oracle.attention(w, nthreads=8)
     dw = DeviceWorkload(w)
     out, lse, dec = dw.run(plan=sda.sda_plan(parts, 64, 2, 2))
-    compare(out, lse, o_ref, l_ref, what=f"64-head plan, {parts} parts", count_flips=True)
+    compare(out, lse, o_ref, l_ref, what=f"64-head plan, {parts} parts")
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
@@ -309,7 +309,7 @@ def test_precision_modes(name, T, precision):
     plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
     plan.precision = precision
     out, lse, _ = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"{name} precision {precision}", count_flips=precision > 1)
+    compare(out, lse, o_ref, l_ref, what=f"{name} precision {precision}", eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
 # ------------------------------------------------------------------ decode tables on the GPU
@@ -469,10 +469,8 @@ def test_whole_token_plan_16_head_groups(name):
     """The head grouping the binding picks for whole-token calls on the fp8 ring kernel (16 heads per
     workgroup): same bar against the oracle."""
     w = wl.make_workload(name, seed=4, T=SMALL_T[name])
-    plan = _whole_plan(w)
-    plan.heads_per_group = sda.whole_token_heads_per_group(
-        plan, w.T, w.H, w.d_qk, [w.cache.fmt, w.xcache.fmt if w.xcache is not None else None])
-    assert plan.heads_per_group == 16
+    plan = auto_plan_for(w)  # the library's choice on these lengths: whole tokens, 16 heads per workgroup
+    assert plan.whole_tokens == 1 and plan.heads_per_group == 16
     _log(f"[whole hb16] {name} T={w.T}")
     o_ref, l_ref = oracle.attention(w, nthreads=8)
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
