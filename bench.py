@@ -6,9 +6,10 @@ split plan, or the decode kernel alone for a whole-token plan. The headline (def
 configuration: 128 decode tokens x 128 heads, d_qk 576 / d_v 512, 656-byte V3.2 records in a 131072-slot
 paged cache, 2048 slots per token, sink on. It is timed on cold buffers: enough independent copies of q,
 the cache, the slot lists and the outputs are rotated that their total exceeds twice the 256 MB MALL, so
-every call reads from HBM. The timed region is exactly --steps steps between two synchronizations; HIP
-events on the launch stream around each decode-kernel launch inside it give the kernel's mean duration for
-the roofline.
+every call reads from HBM. The timed region is exactly --steps back-to-back steps between two
+synchronizations, bracketed by HIP events on the launch stream; with the whole-token plan the library picks
+for it a step is one launch of the decode kernel, so the region also gives that kernel's mean duration for
+the roofline (split plans: the decode kernel is timed the same way over its own back-to-back launches).
 
 Prints one JSON line: query-tokens/s (value), the roofline position of the decode kernel and of the whole
 step, per-configuration results for the five benchmark configurations (hot and cold; the top-k one on both
@@ -22,7 +23,6 @@ import hashlib
 import json
 import math
 import os
-import statistics
 import sys
 import time
 
@@ -36,7 +36,7 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
-               for f in ("sda_decode_ring.hip", "sda_decode_staged.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
+               for f in ("sda_decode_ring.hip", "sda_decode_wide.hip", "sda_decode_staged.hip", "sda_items.h", "sda_sched.hip", "sda_device.h",
                          "sda_internal.h", "sda_v41.hip")]
 CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
 COLD_BYTES = 600e6             # rotated buffer sets exceed twice the MALL
@@ -201,8 +201,10 @@ def roofline(byts, flops, t):
 
 
 class Runner:
-    """Device inputs and launch plumbing of one workload under one plan: the step is the whole op, with HIP
-    events recorded on the launch stream around its decode-kernel launch."""
+    """Device inputs and launch plumbing of one workload under one plan. The step is the whole op: for a
+    whole-token plan one launch of the decode kernel, for a split plan the scheduler, the decode kernel and the
+    combine (the launches sda_sparse_decode_attn makes). Arguments are marshalled once per buffer set, so
+    the host enqueues a step in a few microseconds."""
 
     def __init__(self, w, dw, plan):
         import torch
@@ -223,7 +225,33 @@ class Runner:
         ws = self.dec.workspace
         self.o_acc = ws[:S * w.H * 512 * 4].view(torch.float32).view(S, w.H, 512)
         self.lse_acc = ws[off:off + S * w.H * 4].view(torch.float32).view(S, w.H)
-        self.sets = [(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, self.out, self.lse)]
+        self.set_buffers([(dw.q, dw.cache, dw.lst, dw.xcache, dw.xlst, self.out, self.lse)])
+
+    def set_buffers(self, sets):
+        self.sets = sets
+        self.calls = [self._prepare(st) for st in sets]
+
+    def _prepare(self, st):
+        """(the step's launches, the decode-kernel launch alone) for one buffer set."""
+        sda, w, plan, dec, dw = self.sda, self.w, self.plan, self.dec, self.dw
+        q, c, L, xc, xL, out, lse = st
+        meta, ns = dec.sched_arrays
+        sched = [] if plan.whole_tokens else [sda.prepare_get_sched_meta(w.T, L, xL, plan, meta, ns)]
+        if self.v41:  # Q RoPE, decode, combine with the inverse RoPE and the MXFP8 cast (one call)
+            def v41_call():
+                sda.sparse_decode_attn_v41(q, c, L, xc, xL, dw.sink, w.scale, plan, meta, ns, dec.workspace,
+                                           dw.positions, dw.cos_sin, self.out8, self.osc, lse)
+            decode = sda.prepare_decode_splits(q, c, L, xc, xL, dw.sink, w.scale, plan, meta, ns, dec.workspace,
+                                               None, None)
+            return sched + [v41_call], decode
+        if plan.whole_tokens:  # one launch: the decode kernel writes every token whole
+            call = sda.prepare_sparse_decode_attn(q, c, L, xc, xL, dw.sink, w.scale, plan, None, None, dec.workspace,
+                                                  out, lse)
+            return [call], call
+        decode = sda.prepare_decode_splits(q, c, L, xc, xL, dw.sink, w.scale, plan, meta, ns, dec.workspace, out,
+                                           lse)
+        combine = sda.prepare_combine_splits(self.o_acc, self.lse_acc, ns, dw.sink, out, lse)
+        return sched + [decode, combine], decode
 
     def make_cold_sets(self):
         """Independent copies of q, the caches, the slot lists and the outputs, rotated by the steps so that
@@ -244,57 +272,44 @@ class Runner:
         per_set = (dw.q.numel() * 2 + self.out.numel() * 2 + dw.cache.data.numel() + dw.lst.idx.numel() * 4 +
                    (dw.xcache.data.numel() + dw.xlst.idx.numel() * 4 if dw.xcache is not None else 0))
         nsets = min(64, max(2, int(math.ceil(COLD_BYTES / per_set))))
-        self.sets = [(dw.q.clone(), cache_copy(dw.cache), list_copy(dw.lst), cache_copy(dw.xcache),
-                      list_copy(dw.xlst), torch.empty_like(self.out), torch.empty_like(self.lse))
-                     for _ in range(nsets)]
+        self.set_buffers([(dw.q.clone(), cache_copy(dw.cache), list_copy(dw.lst), cache_copy(dw.xcache),
+                           list_copy(dw.xlst), torch.empty_like(self.out), torch.empty_like(self.lse))
+                          for _ in range(nsets)])
         return nsets, per_set
 
-    def step(self, i, ka=None, kb=None):
-        sda, w, plan, dec = self.sda, self.w, self.plan, self.dec
-        q, c, L, xc, xL, out, lse = self.sets[i % len(self.sets)]
-        meta, ns = dec.sched_arrays
-        if self.v41:  # Q RoPE, decode, combine with the inverse RoPE and the MXFP8 cast (one call)
-            dec.schedule(L, xL)
-            if ka is not None:
-                ka.record()
-            sda.sparse_decode_attn_v41(q, c, L, xc, xL, self.dw.sink, w.scale, plan, meta, ns, dec.workspace,
-                                       self.dw.positions, self.dw.cos_sin, self.out8, self.osc, lse)
-            if kb is not None:
-                kb.record()
-            return
-        if plan.whole_tokens:  # one launch: the decode kernel writes every token whole
-            if ka is not None:
-                ka.record()
-            sda.sparse_decode_attn(q, c, L, xc, xL, self.dw.sink, w.scale, plan, None, None, dec.workspace, out, lse)
-            if kb is not None:
-                kb.record()
-            return
-        # split plan: scheduler, decode kernel, combine (the launches sda_sparse_decode_attn makes)
-        dec.schedule(L, xL)
-        if ka is not None:
-            ka.record()
-        sda.decode_splits(q, c, L, xc, xL, self.dw.sink, w.scale, plan, meta, ns, dec.workspace, out, lse)
-        if kb is not None:
-            kb.record()
-        sda.combine_splits(self.o_acc, self.lse_acc, ns, self.dw.sink, out, lse)
-
     def time(self, steps, warmup):
-        """Mean step (ms) over exactly `steps` steps between two synchronizations, and the decode kernel's mean
-        and median duration (ms) from the events around its launch in each timed step (V4.1: the whole call)."""
+        """(mean step, mean decode-kernel duration, host enqueue time per step), all in ms. The step is timed
+        over exactly `steps` back-to-back steps between two synchronizations, with HIP events on the launch
+        stream bracketing them; the decode kernel is the step itself for a whole-token plan (one launch), and
+        otherwise timed the same way over `steps` back-to-back decode-kernel launches."""
         torch = self.torch
+        n = len(self.calls)
         for i in range(warmup):
-            self.step(i)
-        ka = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        kb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            for f in self.calls[i % n][0]:
+                f()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            for f in self.calls[i % n][0]:
+                f()
+        e1.record()
+        h1 = time.perf_counter()
+        torch.cuda.synchronize()
+        step = e0.elapsed_time(e1) / steps
+        host = (h1 - h0) * 1e3 / steps
+        if self.plan.whole_tokens and not self.v41:
+            return step, step, host
+        for i in range(min(warmup, 5)):
+            self.calls[i % n][1]()
         torch.cuda.synchronize()
         e0.record()
         for i in range(steps):
-            self.step(i, ka[i], kb[i])
+            self.calls[i % n][1]()
         e1.record()
         torch.cuda.synchronize()
-        kern = [a.elapsed_time(b) for a, b in zip(ka, kb)]
-        return e0.elapsed_time(e1) / steps, sum(kern) / steps, statistics.median(kern)
+        return step, e0.elapsed_time(e1) / steps, host
 
 
 def plan_dict(plan):
@@ -308,22 +323,22 @@ def measure(w, dw, plan, steps, warmup, cold=True):
     and of the decode kernel."""
     byts, flops, rows = algorithmic_work(w)
     r = Runner(w, dw, plan)
-    st_h, k_h, km_h = r.time(steps, warmup)
+    st_h, k_h, ho_h = r.time(steps, warmup)
     res = {"plan": plan_dict(plan), "alg_bytes": byts, "alg_flops": flops, "valid_rows": rows,
            "hot": {"step_us": round(st_h * 1e3, 2), "kernel_us": round(k_h * 1e3, 2),
-                   "kernel_us_median": round(km_h * 1e3, 2), "query_tokens_per_s": round(w.T / (st_h / 1e3), 1),
+                   "host_enqueue_us": round(ho_h * 1e3, 2), "query_tokens_per_s": round(w.T / (st_h / 1e3), 1),
                    "roofline_step": roofline(byts, flops, st_h / 1e3),
                    "roofline_kernel": roofline(byts, flops, k_h / 1e3)}}
     if cold:
         nsets, per_set = r.make_cold_sets()
-        st_c, k_c, km_c = r.time(steps, max(warmup, nsets))
+        st_c, k_c, ho_c = r.time(steps, max(warmup, nsets))
         res["cold"] = {"step_us": round(st_c * 1e3, 2), "kernel_us": round(k_c * 1e3, 2),
-                       "kernel_us_median": round(km_c * 1e3, 2), "query_tokens_per_s": round(w.T / (st_c / 1e3), 1),
+                       "host_enqueue_us": round(ho_c * 1e3, 2), "query_tokens_per_s": round(w.T / (st_c / 1e3), 1),
                        "tflops": round(flops / (st_c / 1e3) / 1e12, 2), "gbps": round(byts / (st_c / 1e3) / 1e9, 1),
                        "roofline_step": roofline(byts, flops, st_c / 1e3),
                        "roofline_kernel": roofline(byts, flops, k_c / 1e3),
                        "buffer_sets": nsets, "set_mb": round(per_set / 1e6, 1)}
-        r.sets = r.sets[:1]
+        r.set_buffers(r.sets[:1])
     return res, r
 
 
@@ -391,8 +406,9 @@ def main():
     if not args.hot:
         nsets, per_set = r.make_cold_sets()
         log(f"[bench] cold: {nsets} buffer sets of {per_set / 1e6:.1f} MB")
-    ms_step, ms_kern, ms_kern_med = r.time(args.steps, max(args.warmup, len(r.sets)))
-    log(f"[bench] step {ms_step * 1e3:.2f} us, decode kernel {ms_kern * 1e3:.2f} us (median {ms_kern_med * 1e3:.2f})")
+    ms_step, ms_kern, ms_host = r.time(args.steps, max(args.warmup, len(r.sets)))
+    log(f"[bench] step {ms_step * 1e3:.2f} us, decode kernel {ms_kern * 1e3:.2f} us, host enqueue "
+        f"{ms_host * 1e3:.2f} us per step")
     t_step, t_kern = ms_step / 1e3, ms_kern / 1e3
     sha = kernel_sha()
     roof = roofline(byts, flops, t_kern)
@@ -421,7 +437,7 @@ def main():
         "tflops": round(flops / t_step / 1e12, 2),
         "gbps": round(byts / t_step / 1e9, 1),
         "decode_kernel_us": round(ms_kern * 1e3, 2),
-        "decode_kernel_us_median": round(ms_kern_med * 1e3, 2),
+        "host_enqueue_us": round(ms_host * 1e3, 2),
         "roofline": roof_k,
         "roofline_step": roofline(byts, flops, t_step),
         "alg_bytes": byts,

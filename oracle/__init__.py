@@ -59,6 +59,7 @@ def lib():
                                ctypes.c_int, ctypes.c_int, ctypes.POINTER(OrcCache), ctypes.POINTER(OrcList),
                                ctypes.POINTER(OrcCache), ctypes.POINTER(OrcList), ctypes.c_void_p, ctypes.c_float,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.orc_attn_abs.argtypes = L.orc_attn.argtypes[:-1] + [ctypes.c_void_p, ctypes.c_int]
         L.orc_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.orc_bf16_rne.argtypes = [ctypes.c_float]
@@ -111,8 +112,10 @@ def decode_slot(cache, sid: int) -> Optional[np.ndarray]:
     return k if ok else None
 
 
-def attention(w, tokens: Optional[slice] = None, nthreads: int = 1, sink="default", scale: Optional[float] = None):
-    """Oracle out [T, H, d_v] (float64) and lse [T, H] for workload `w` (or a slice of its tokens)."""
+def attention(w, tokens: Optional[slice] = None, nthreads: int = 1, sink="default", scale: Optional[float] = None,
+              with_abs: bool = False):
+    """Oracle out [T, H, d_v] (float64) and lse [T, H] for workload `w` (or a slice of its tokens); with_abs adds
+    out_abs [T, H, d_v], the weighted mean of the rows' magnitudes (orc_attn_abs)."""
     t0, t1 = (0, w.T) if tokens is None else (tokens.start or 0, tokens.stop if tokens.stop is not None else w.T)
     T = t1 - t0
     keep = []
@@ -129,14 +132,16 @@ def attention(w, tokens: Optional[slice] = None, nthreads: int = 1, sink="defaul
     keep.append(snk)
     out = np.zeros((T, w.H, w.d_v), dtype=np.float64)
     lse = np.zeros((T, w.H), dtype=np.float64)
-    rc = lib().orc_attn(q.ctypes.data, q.shape[1] * q.shape[2], q.shape[2], T, w.H, w.d_qk, w.d_v,
-                        ctypes.byref(cs), ctypes.byref(ls),
-                        ctypes.byref(xcs) if xcs is not None else None, ctypes.byref(xls) if xls is not None else None,
-                        _ptr(snk), ctypes.c_float(w.scale if scale is None else scale),
-                        out.ctypes.data, lse.ctypes.data, int(nthreads))
+    oabs = np.zeros((T, w.H, w.d_v), dtype=np.float64) if with_abs else None
+    rc = lib().orc_attn_abs(q.ctypes.data, q.shape[1] * q.shape[2], q.shape[2], T, w.H, w.d_qk, w.d_v,
+                            ctypes.byref(cs), ctypes.byref(ls),
+                            ctypes.byref(xcs) if xcs is not None else None,
+                            ctypes.byref(xls) if xls is not None else None,
+                            _ptr(snk), ctypes.c_float(w.scale if scale is None else scale),
+                            out.ctypes.data, lse.ctypes.data, _ptr(oabs), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return out, lse
+    return (out, lse, oabs) if with_abs else (out, lse)
 
 
 def rope_q(q: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray) -> np.ndarray:
@@ -170,15 +175,15 @@ def mxfp8_out(out: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray):
 def attention_v41(w, tokens: Optional[slice] = None, nthreads: int = 1):
     """The V4.1 decode of workload `w` (which carries `rope`): Q RoPE, attention, inverse RoPE and the MXFP8
     output cast. Returns (codes [T, H, 512], scale bytes [T, H, 16], lse [T, H], out [T, H, 512] float64 before
-    the cast) for all tokens or a slice of them."""
+    the cast, out_abs [T, H, 512] of orc_attn_abs) for all tokens or a slice of them."""
     import copy
     assert w.rope is not None and w.d_qk == 512
     w2 = copy.copy(w)
     w2.q = rope_q(w.q, w.rope.positions, w.rope.cos_sin)
-    out, lse = attention(w2, tokens=tokens, nthreads=nthreads)
+    out, lse, oabs = attention(w2, tokens=tokens, nthreads=nthreads, with_abs=True)
     pos = w.rope.positions if tokens is None else w.rope.positions[tokens]
     codes, scales = mxfp8_out(out, pos, w.rope.cos_sin)
-    return codes, scales, lse, out
+    return codes, scales, lse, out, oabs
 
 
 def merge(o_parts: np.ndarray, lse_parts: np.ndarray, sink: Optional[np.ndarray]):

@@ -151,6 +151,7 @@ typedef struct {
   float scale;
   double* out;
   double* lse;
+  double* out_abs;  /* optional: sum_i w_i |v_i| / den, with the weights of out */
   int t_begin, t_step;
 } job_t;
 
@@ -174,10 +175,13 @@ static void token_heads(const job_t* jb, int t, const double* rows, int n, doubl
   int h, i, d;
   for (h = 0; h < jb->H; h++) {
     double* o = jb->out + ((int64_t)t * jb->H + h) * jb->d_v;
+    double* oa = jb->out_abs ? jb->out_abs + ((int64_t)t * jb->H + h) * jb->d_v : NULL;
     double* lse = jb->lse + (int64_t)t * jb->H + h;
     int has_sink = jb->sink != NULL;
     double sk = has_sink ? (double)jb->sink[h] : -INFINITY;
     for (d = 0; d < jb->d_v; d++) o[d] = 0.0;
+    if (oa)
+      for (d = 0; d < jb->d_v; d++) oa[d] = 0.0;
     for (d = 0; d < jb->d_qk; d++) qd[d] = orc_bf16(jb->q[(int64_t)t * jb->qst + (int64_t)h * jb->qsh + d]);
     if (n == 0) {            /* no rows: zero output; the sink alone is the log-sum-exp */
       *lse = has_sink ? sk : -INFINITY;
@@ -201,8 +205,12 @@ static void token_heads(const job_t* jb, int t, const double* rows, int n, doubl
       const double* v = rows + (int64_t)i * jb->d_qk;
       den += w;
       for (d = 0; d < jb->d_v; d++) o[d] += w * v[d];
+      if (oa)
+        for (d = 0; d < jb->d_v; d++) oa[d] += w * fabs(v[d]);
     }
     for (d = 0; d < jb->d_v; d++) o[d] /= den;
+    if (oa)
+      for (d = 0; d < jb->d_v; d++) oa[d] /= den;
     *lse = M + log(den);
   }
 }
@@ -227,6 +235,13 @@ static void* run_job(void* arg) {
 int orc_attn(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
              const orc_cache* cache, const orc_list* list, const orc_cache* xcache, const orc_list* xlist,
              const float* sink, float scale, double* out, double* lse, int nthreads) {
+  return orc_attn_abs(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, xcache, xlist, sink, scale, out, lse,
+                      NULL, nthreads);
+}
+
+int orc_attn_abs(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                 const orc_cache* cache, const orc_list* list, const orc_cache* xcache, const orc_list* xlist,
+                 const float* sink, float scale, double* out, double* lse, double* out_abs, int nthreads) {
   if (!q || !cache || !list || !out || !lse || T < 0 || H <= 0) return -1;
   if ((xcache == NULL) != (xlist == NULL)) return -1;
   if (orc_record_dims(cache->format) != d_qk) return -1;
@@ -238,7 +253,7 @@ int orc_attn(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, i
   base.T = T; base.H = H; base.d_qk = d_qk; base.d_v = d_v;
   base.c[0] = cache; base.l[0] = list; base.nl = 1;
   if (xcache) { base.c[1] = xcache; base.l[1] = xlist; base.nl = 2; }
-  base.sink = sink; base.scale = scale; base.out = out; base.lse = lse;
+  base.sink = sink; base.scale = scale; base.out = out; base.lse = lse; base.out_abs = out_abs;
   if (nthreads <= 1 || T <= 1) {
     base.t_begin = 0; base.t_step = 1;
     run_job(&base);

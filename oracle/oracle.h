@@ -66,6 +66,14 @@ int orc_attn(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, i
              const orc_cache* cache, const orc_list* list, const orc_cache* xcache, const orc_list* xlist,
              const float* sink, float scale, double* out, double* lse, int nthreads);
 
+/* orc_attn plus out_abs [T][H][d_v] (nullable): sum_i exp(z_i - M) |v_i| / den, the weighted mean of the
+ * rows' magnitudes under the same weights (zero for an empty token). It is the scale that a relative error
+ * in the weights moves the output by (|sum_i w_i d_i v_i| <= max |d_i| out_abs), which the tests' rounding
+ * tolerance is stated in; it is no part of the method. */
+int orc_attn_abs(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                 const orc_cache* cache, const orc_list* list, const orc_cache* xcache, const orc_list* xlist,
+                 const float* sink, float scale, double* out, double* lse, double* out_abs, int nthreads);
+
 /* ---- V4.1 decode prologue and epilogue (vLLM swapab_decode_attn page: Q RoPE
  * in stage_inputs, inverse RoPE and the MXFP8 output cast in device kernel step
  * 9). Both follow the page's single-precision steps, so that the quantized

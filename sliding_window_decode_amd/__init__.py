@@ -195,20 +195,68 @@ def get_sched_meta_host(T: int, lens, width: int, extra_lens, extra_width: int, 
     return meta, ns
 
 
-def _decode_call(fn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits, workspace,
-                 out, lse, stream):
+def _decode_args(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits, workspace, out,
+                 lse, stream):
     T, H, d_qk = q.shape
     d_v = 512 if out is None else out.shape[-1]
     cc, cl = cache.c(), lst.c()
     xc = extra_cache.c() if extra_cache is not None else None
     xl = extra_lst.c() if extra_lst is not None else None
-    _check(fn(
-        _ptr(q), q.stride(0), q.stride(1), T, H, d_qk, d_v, ctypes.byref(cc), ctypes.byref(cl),
-        ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
-        _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
-        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _ptr(out), 0 if out is None else out.stride(0), 0 if out is None else out.stride(1), _ptr(lse),
-        0 if lse is None else lse.stride(0), _stream(stream)))
+    return (_ptr(q), q.stride(0), q.stride(1), T, H, d_qk, d_v, ctypes.byref(cc), ctypes.byref(cl),
+            ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
+            _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
+            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(out), 0 if out is None else out.stride(0), 0 if out is None else out.stride(1), _ptr(lse),
+            0 if lse is None else lse.stride(0), _stream(stream))
+
+
+def _decode_call(fn, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits, workspace,
+                 out, lse, stream):
+    _check(fn(*_decode_args(q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta, num_splits,
+                            workspace, out, lse, stream)))
+
+
+def _prepared(fn, args):
+    def call():
+        rc = fn(*args)
+        if rc != SDA_OK:
+            _check(rc)
+    return call
+
+
+def prepare_sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache],
+                               extra_lst: Optional[SlotList], attn_sink, scale: float, plan: sda_plan, meta,
+                               num_splits, workspace, out, lse, stream=None):
+    """sparse_decode_attn with its arguments marshalled once: returns a callable that enqueues the op on the
+    stream current now (for launch loops; the tensors must stay alive)."""
+    return _prepared(lib().sda_sparse_decode_attn, _decode_args(q, cache, lst, extra_cache, extra_lst, attn_sink,
+                                                                scale, plan, meta, num_splits, workspace, out, lse,
+                                                                stream))
+
+
+def prepare_decode_splits(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],
+                          attn_sink, scale: float, plan: sda_plan, meta, num_splits, workspace, out, lse, stream=None):
+    """decode_splits with its arguments marshalled once (see prepare_sparse_decode_attn)."""
+    return _prepared(lib().sda_decode_splits, _decode_args(q, cache, lst, extra_cache, extra_lst, attn_sink, scale,
+                                                           plan, meta, num_splits, workspace, out, lse, stream))
+
+
+def prepare_get_sched_meta(T: int, lst: SlotList, extra: Optional[SlotList], plan: sda_plan, meta, num_splits,
+                           stream=None):
+    """get_sched_meta with its arguments marshalled once (see prepare_sparse_decode_attn)."""
+    cl = lst.c()
+    xl = extra.c() if extra is not None else None
+    return _prepared(lib().sda_get_sched_meta, (T, ctypes.byref(cl), ctypes.byref(xl) if xl is not None else None,
+                                                ctypes.byref(plan), _ptr(meta), _ptr(num_splits), _stream(stream)))
+
+
+def prepare_combine_splits(o_accum, lse_accum, num_splits, attn_sink, out, lse, stream=None):
+    """combine_splits with its arguments marshalled once (see prepare_sparse_decode_attn)."""
+    T = num_splits.shape[0] - 1
+    H, d_v = out.shape[1], out.shape[2]
+    return _prepared(lib().sda_combine_splits, (T, H, d_v, _ptr(o_accum), _ptr(lse_accum), _ptr(num_splits),
+                                                _ptr(attn_sink), _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+                                                lse.stride(0), _stream(stream)))
 
 
 def sparse_decode_attn(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], extra_lst: Optional[SlotList],

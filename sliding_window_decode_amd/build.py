@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libsda.so")
-SOURCES = ["sda_decode_ring.hip", "sda_decode_staged.hip", "sda_sched.hip", "sda_v41.hip", "sda_api.cpp"]
+SOURCES = ["sda_decode_ring.hip", "sda_decode_wide.hip", "sda_decode_staged.hip", "sda_sched.hip", "sda_v41.hip", "sda_api.cpp"]
 
 # packed-fp32 instructions are kept out of the generated code on purpose
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

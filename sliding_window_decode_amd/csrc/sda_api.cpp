@@ -150,6 +150,8 @@ hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_gro
   // 592-byte ring rows leave no room for two 16-head workgroups per CU), else the staged kernel
   const int m1 = (p.lst[0].format == SDA_MODEL1_584) + (p.nlists > 1 && p.lst[1].format == SDA_MODEL1_584);
   const bool staged = fp4 || (m1 > 0 && (m1 < p.nlists || heads_per_group < 32)) || (ue > 0 && ue < p.nlists);
+  // 576-dim records (every list SDA_V32_656) with 64 heads per workgroup: the 32x32-product kernel
+  if (d_qk == 576 && heads_per_group == 64) return launch_decode_wide(p, num_parts, precision, stream);
   // the register-staged kernel takes at most 32 heads per workgroup
   return staged ? launch_decode_staged(p, num_parts, heads_per_group > 32 ? 32 : heads_per_group, d_qk, precision,
                                        stream)

@@ -12,13 +12,15 @@ OUT_MAX_ABS = 1e-2
 OUT_REL_L2 = 5e-3
 LSE_MAX_ABS = 1e-3
 
-# Relative error budget of the kernel's fp32 result before its rounding to bf16. With two or three bf16
-# terms of the softmax weights in P.V, each weight is within 2^-18 of its fp32 value; the other steps are
-# fp32 operations on exact bf16 products (score sums over at most 18 MFMA chunks, the scale fold, exp2,
-# the weight-times-scale product, the P.V sums and the final normalization), each rounding within 2^-24
-# of its result, together below 2^-19 for outputs that are weighted means of rows of like magnitude;
-# 2^-16 leaves a factor of four. With one term each weight is rounded once to bf16 (2^-9): 2^-8.
-EPS_FP32 = 2.0 ** -16
+# Error budget of the kernel's fp32 result before its rounding to bf16, relative to out_abs (the weighted
+# mean of the rows' magnitudes under the softmax weights, oracle.attention(..., with_abs=True)). Relative
+# errors d_i in the weights move the output by sum_i w_i (d_i - mean d) v_i, at most 2 max|d| out_abs.
+# With two or three bf16 terms of P' a weight is within 2^-18 of its fp32 value; exp2 adds 2^-22; a
+# score's fp32 sum (18 MFMA chunks, 4 scale folds and the scale: 23 roundings of partial sums below 2^4.5
+# in log2 units here) is off by at most 2^-15 in log2 units, a relative 2^-15.5 in its weight; the P.V sums
+# (at most 160 chunks of 16 rows) add 2^-16.7 of out_abs. Together below 2^-14: EPS_FP32. With one term
+# each weight is rounded once to bf16 (2^-9), so 2 x 2^-9: EPS_P1.
+EPS_FP32 = 2.0 ** -14
 EPS_P1 = 2.0 ** -8
 
 
@@ -41,13 +43,13 @@ def _e4m3_rne(y: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-def _inverse_rope_f64(out: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray):
+def _inverse_rope_f64(out: np.ndarray, oabs: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray):
     """out [T, H, 512] with dims 448..511 rotated back per GPT-J pair in float64 (positions outside the table:
     unrotated), for locating the cast's decision points (the oracle takes the cast itself in fp32). Returns
-    (x, m): the rotated values and the magnitudes their errors scale with, |e cos| + |sin o| for a rotated
-    dim and |x| for the others."""
+    (x, m): the rotated values and the magnitudes their errors scale with: out_abs for an unrotated dim,
+    |cos| out_abs_e + |sin| out_abs_o for a rotated one."""
     x = np.array(out, dtype=np.float64)
-    m = np.abs(x)
+    m = np.array(oabs, dtype=np.float64)
     pos = np.asarray(positions, dtype=np.int64)
     ok = (pos >= 0) & (pos < cos_sin.shape[0])
     c = np.ones((len(pos), 32))
@@ -56,23 +58,24 @@ def _inverse_rope_f64(out: np.ndarray, positions: np.ndarray, cos_sin: np.ndarra
     sn[ok] = cos_sin[pos[ok], 32:64]
     c, sn = c[:, None, :], sn[:, None, :]
     e, o = out[..., 448::2], out[..., 449::2]
+    ae, ao = oabs[..., 448::2], oabs[..., 449::2]
     x[..., 448::2] = e * c + sn * o
     x[..., 449::2] = o * c - sn * e
-    m[..., 448::2] = np.abs(e * c) + np.abs(sn * o)
-    m[..., 449::2] = np.abs(o * c) + np.abs(sn * e)
+    m[..., 448::2] = np.abs(c) * ae + np.abs(sn) * ao
+    m[..., 449::2] = np.abs(c) * ao + np.abs(sn) * ae
     return x, m
 
 
 def compare_v41(codes_gpu, scales_gpu, lse_gpu, ref, positions, cos_sin, what="", exact=False, eps=EPS_FP32):
     """MXFP8 output against the oracle's cast of its own result, element by element.
 
-    ref = oracle.attention_v41(...) (codes, scale bytes, lse, fp64 attention result). Both sides take the cast's
-    decisions in fp32 from attention results that differ by the kernel's error (eps relative). Per 32-dim chunk
+    ref = oracle.attention_v41(...) (codes, scale bytes, lse, fp64 attention result, its out_abs). Both sides
+    take the cast's decisions in fp32 from attention results that differ by the kernel's error (eps out_abs). Per 32-dim chunk
     with amax = max(max |x|, 1e-10) over the inverse-rotated oracle values x, the GPU's scale byte must be the
     ue8m0 rounding up of some value within eps of amax / 448; per element, with the GPU's own scale byte b, its
     code must decode to the e4m3 rounding of some value within eps of x 2^(127 - b). The window is checked to
     hold the oracle's own decisions. LSE within 1e-3. exact=True: codes and scales bit-identical."""
-    codes_ref, scales_ref, l_ref, out_ref = ref
+    codes_ref, scales_ref, l_ref, out_ref, oabs_ref = ref
     cg = codes_gpu.cpu().numpy() if hasattr(codes_gpu, "cpu") else codes_gpu
     sg = scales_gpu.cpu().numpy() if hasattr(scales_gpu, "cpu") else scales_gpu
     lg = lse_gpu.float().cpu().numpy().astype(np.float64)
@@ -82,7 +85,7 @@ def compare_v41(codes_gpu, scales_gpu, lse_gpu, ref, positions, cos_sin, what=""
     assert np.all((cg & 0x7F) != 0x7F), f"{what}: NaN codes"
     # kernel error: eps times each element's magnitude m; the fp32 rotation adds at most 2^-21 of the chunk's
     # amax (two products of values within sqrt(2) amax, each rounded once, then their sum)
-    x, m = _inverse_rope_f64(out_ref, positions, cos_sin)
+    x, m = _inverse_rope_f64(out_ref, oabs_ref, positions, cos_sin)
     T, H, _ = x.shape
     err = eps * m + 2.0 ** -21 * np.repeat(np.abs(x).reshape(T, H, 16, 32).max(-1), 32, axis=-1)
     amax_lo = np.maximum((np.abs(x) - err).reshape(T, H, 16, 32).max(-1), 1e-10)
@@ -121,15 +124,15 @@ def eps_for(plan) -> float:
     return EPS_P1 if plan is not None and plan.precision == 1 else EPS_FP32
 
 
-def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", eps=EPS_FP32):
+def compare(out_gpu, lse_gpu, o_ref, l_ref, o_abs, tokens=None, what="", eps=EPS_FP32):
     """Assert the tolerances element by element; returns a dict of the error figures.
 
     out: each element within 1e-2 of the round-to-nearest-even bf16 of the fp64 oracle value x, or else
-    equal to the bf16 rounding of some value within eps |x| of x: where x lies within the kernel's fp32
-    error budget of a bf16 rounding midpoint, either neighbour is a correct rounding of a result that
-    precise, and where |x| >= 2 one bf16 ulp (2^-6 and up) exceeds 1e-2 by itself. No count of such
-    elements is allowed for; each is checked on its own. rel-L2 <= 5e-3 over all elements. lse: within
-    1e-3 absolute, infinities exact (with their signs)."""
+    equal to the bf16 rounding of some value within eps o_abs of x (o_abs: the oracle's weighted mean of the
+    rows' magnitudes): where x lies within the kernel's fp32 error budget of a bf16 rounding midpoint,
+    either neighbour is a correct rounding of a result that precise, and where |x| >= 2 one bf16 ulp (2^-6
+    and up) exceeds 1e-2 by itself. No count of such elements is allowed for; each is checked on its own.
+    rel-L2 <= 5e-3 over all elements. lse: within 1e-3 absolute, infinities exact (with their signs)."""
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     lg = lse_gpu.float().cpu().numpy().astype(np.float64)
     if tokens is not None:
@@ -147,8 +150,10 @@ def compare(out_gpu, lse_gpu, o_ref, l_ref, tokens=None, what="", eps=EPS_FP32):
     lse_err = float(np.abs(lg[~inf_ref] - l_ref[~inf_ref]).max()) if (~inf_ref).any() else 0.0
     over = diff > OUT_MAX_ABS
     # the bf16 values that round some y with |y - x| <= eps |x| (rounding is monotonic: all between these two)
-    lo = oracle.bf16_rne(o_ref - eps * np.abs(o_ref))
-    hi = oracle.bf16_rne(o_ref + eps * np.abs(o_ref))
+    o_abs = np.asarray(o_abs, dtype=np.float64)
+    assert o_abs.shape == o_ref.shape, f"{what}: out_abs shape {o_abs.shape} against {o_ref.shape}"
+    lo = oracle.bf16_rne(o_ref - eps * o_abs)
+    hi = oracle.bf16_rne(o_ref + eps * o_abs)
     in_window = (got >= lo) & (got <= hi)
     bad = over & ~in_window
     info = dict(max_abs=max_abs, rel_l2=rel_l2, lse_max_abs=lse_err, midpoint_roundings=int(over.sum()),

@@ -34,10 +34,10 @@ SMALL_T = {"c1_tiny_swa": 4, "c2_swa_h128": 6, "c3_swa_fp8extra": 12, "c4_swa_nv
 def test_config_parity_reduced_tokens(name, seed):
     _log(f"[parity] {name} seed={seed} T={SMALL_T[name]}")
     w = wl.make_workload(name, seed=seed, T=SMALL_T[name])
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     dw = DeviceWorkload(w)
     out, lse, dec = dw.run()
-    info = compare(out, lse, o_ref, l_ref, what=f"{name}/{seed}")
+    info = compare(out, lse, o_ref, l_ref, o_abs, what=f"{name}/{seed}")
     _log(f"  {dec.plan} {info}")
 
 
@@ -59,8 +59,8 @@ def test_config_parity_full_size(name, schedule):
     _log(f"[parity-full] {name} T={w.T} {plan}")
     dw = DeviceWorkload(w)
     out, lse, dec = dw.run(plan=plan)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
-    info = compare(out, lse, o_ref, l_ref, what=f"{name} full size, {schedule} plan")
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
+    info = compare(out, lse, o_ref, l_ref, o_abs, what=f"{name} full size, {schedule} plan")
     _log(f"  {info}")
 
 
@@ -70,10 +70,10 @@ def test_config_parity_full_size(name, schedule):
 def test_any_plan_same_result(parts, hb, F):
     w = wl.small_workload(3, wl.FP8_528, wl.NVFP4_288, T=9, H=32, width=128, xwidth=300, num_slots=4096,
                           sink=True, p_invalid=0.05, lens_lo=1)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     dw = DeviceWorkload(w)
     out, lse, dec = dw.run(plan=sda.sda_plan(parts, hb, F, 3))
-    compare(out, lse, o_ref, l_ref, what=f"plan {parts}/{hb}/{F}")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"plan {parts}/{hb}/{F}")
 
 
 # FP8_UE8M0 lists: both lists of the format run the ring kernel built for it; mixed with another
@@ -85,11 +85,11 @@ def test_any_plan_same_result(parts, hb, F):
 def test_ue8m0_lists(fmt, xfmt, H, precision):
     w = wl.small_workload(40 + 7 * fmt + (xfmt or 0) + H, fmt, xfmt, T=9, H=H, width=140,
                           xwidth=300 if xfmt is not None else 0, num_slots=2048, sink=True, p_invalid=0.05)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0)
     plan.precision = precision
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"ue8m0 {fmt}/{xfmt} H={H} precision {precision}",
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"ue8m0 {fmt}/{xfmt} H={H} precision {precision}",
             eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
@@ -104,11 +104,11 @@ def test_model1_lists(fmt, xfmt, H, precision):
     w = wl.small_workload(90 + 7 * fmt + (xfmt or 0) + H, fmt, xfmt, T=9, H=H, width=140,
                           xwidth=300 if xfmt is not None else 0, num_slots=2048, sink=True, p_invalid=0.05,
                           page_size=16)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, w.xlst.width if w.xlst is not None else 0)
     plan.precision = precision
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"model1 {fmt}/{xfmt} H={H} precision {precision}",
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"model1 {fmt}/{xfmt} H={H} precision {precision}",
             eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
@@ -145,10 +145,10 @@ def test_model1_bf16_dims_are_values(H):
 def test_64_head_workgroups(fmt, xfmt, H, parts):
     w = wl.small_workload(70 + fmt + parts, fmt, xfmt, T=7, H=H, width=150, xwidth=260 if xfmt is not None else 0,
                           num_slots=2048, sink=True, p_invalid=0.05, lens_lo=0)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     dw = DeviceWorkload(w)
     out, lse, dec = dw.run(plan=sda.sda_plan(parts, 64, 2, 2))
-    compare(out, lse, o_ref, l_ref, what=f"64-head plan, {parts} parts")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"64-head plan, {parts} parts")
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
@@ -157,28 +157,28 @@ def test_64_head_workgroups(fmt, xfmt, H, parts):
 def test_heads_and_formats(H, fmt):
     w = wl.small_workload(10 + H + fmt, fmt, None, T=3, H=H, width=200, num_slots=1024, sink=(H % 32 == 0),
                           p_invalid=0.1, lens_lo=0)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     out, lse, _ = DeviceWorkload(w).run()
-    compare(out, lse, o_ref, l_ref, what=f"H={H} fmt={fmt}")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"H={H} fmt={fmt}")
 
 
 @pytest.mark.parametrize("fmt,xfmt", [(wl.FP8_SLOTSCALE, wl.NVFP4_288), (wl.NVFP4_288, wl.FP8_SLOTSCALE),
                                       (wl.FP8_528, wl.FP8_SLOTSCALE), (wl.V32_656, wl.V32_656)])
 def test_mixed_list_formats(fmt, xfmt):
     w = wl.small_workload(40 + fmt, fmt, xfmt, T=5, H=16, width=96, xwidth=160, num_slots=2048, sink=True)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     out, lse, _ = DeviceWorkload(w).run()
-    compare(out, lse, o_ref, l_ref, what=f"mixed {fmt}/{xfmt}")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"mixed {fmt}/{xfmt}")
 
 
 # ------------------------------------------------------------------ edge cases
 
 def _run_cmp(w, what, plan=None, sink="default"):
-    o_ref, l_ref = oracle.attention(w, nthreads=8, sink=sink)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, sink=sink, with_abs=True)
     dw = DeviceWorkload(w)
     snk = "default" if isinstance(sink, str) else (None if sink is None else torch.from_numpy(sink).cuda())
     out, lse, _ = dw.run(plan=plan, sink=snk)
-    return compare(out, lse, o_ref, l_ref, what=what), out, lse
+    return compare(out, lse, o_ref, l_ref, o_abs, what=what), out, lse
 
 
 @pytest.mark.parametrize("sink", [False, True])
@@ -274,15 +274,15 @@ def test_extreme_logits():
     w2 = copy.deepcopy(w)
     qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float() * 8.0
     w2.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    o_ref, l_ref = oracle.attention(w2, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w2, nthreads=8, with_abs=True)
     out, lse, _ = DeviceWorkload(w2).run()
-    info = compare(out, lse, o_ref, l_ref, what="extreme logits")
+    info = compare(out, lse, o_ref, l_ref, o_abs, what="extreme logits")
     _log(f"  extreme logits: {info}")
 
 
 def test_strided_q_and_out():
     w = wl.small_workload(63, wl.FP8_528, None, T=5, H=32, width=100, sink=True)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     dw = DeviceWorkload(w)
     qbig = torch.zeros((w.T, w.H + 3, 512 + 64), dtype=torch.bfloat16, device="cuda")
     qbig[:, :w.H, :512] = dw.q
@@ -292,7 +292,7 @@ def test_strided_q_and_out():
     lbig = torch.full((w.T, w.H + 5), 7.0, dtype=torch.float32, device="cuda")
     lse = lbig[:, :w.H]
     dw.run(q=q, out=out, lse=lse)
-    compare(out, lse, o_ref, l_ref, what="strided")
+    compare(out, lse, o_ref, l_ref, o_abs, what="strided")
     assert torch.all(obig[:, w.H:, :] == 7.0) and torch.all(obig[:, :, 512:] == 7.0)
     assert torch.all(lbig[:, w.H:] == 7.0)
 
@@ -304,12 +304,12 @@ def test_precision_modes(name, T, precision):
     """Every P precision (one, two (the default) or three bf16 terms) on every kernel path; the single
     term mode may flip more outputs of magnitude >= 2 by one bf16 ulp."""
     w = wl.make_workload(name, seed=4, T=T)
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     X = w.xlst.width if w.xlst is not None else 0
     plan = sda.make_plan(w.T, w.H, w.d_qk, w.lst.width, X)
     plan.precision = precision
     out, lse, _ = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"{name} precision {precision}", eps=EPS_P1 if precision == 1 else EPS_FP32)
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"{name} precision {precision}", eps=EPS_P1 if precision == 1 else EPS_FP32)
 
 
 # ------------------------------------------------------------------ decode tables on the GPU
@@ -391,7 +391,7 @@ def test_combine_splits_against_oracle_merge():
             o, l = oracle.attention(pw, sink=None)
             o_parts.append(o[0])
             l_parts.append(l[0])
-        refs.append(oracle.attention(tw))
+        refs.append(oracle.attention(tw, with_abs=True))
     ns = np.concatenate([[0], np.cumsum(nparts)]).astype(np.int32)
     o_acc = torch.from_numpy(np.array(o_parts, dtype=np.float32)).cuda()
     l_acc = torch.from_numpy(np.array(l_parts, dtype=np.float32)).cuda()
@@ -401,7 +401,8 @@ def test_combine_splits_against_oracle_merge():
     torch.cuda.synchronize()
     o_ref = np.concatenate([r[0] for r in refs])
     l_ref = np.concatenate([r[1] for r in refs])
-    compare(out, lse, o_ref, l_ref, what="combine")
+    o_abs = np.concatenate([r[2] for r in refs])
+    compare(out, lse, o_ref, l_ref, o_abs, what="combine")
 
 
 def test_repeat_runs_are_bitwise_identical():
@@ -457,24 +458,24 @@ def test_whole_token_plan_parity(name):
     (C3, C4)."""
     w = wl.make_workload(name, seed=3, T=SMALL_T[name])
     _log(f"[whole] {name} T={w.T}")
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     out, lse, dec = DeviceWorkload(w).run(plan=_whole_plan(w))
     assert dec.plan.whole_tokens
-    info = compare(out, lse, o_ref, l_ref, what=f"{name} whole tokens")
+    info = compare(out, lse, o_ref, l_ref, o_abs, what=f"{name} whole tokens")
     _log(f"  {dec.plan} {info}")
 
 
 @pytest.mark.parametrize("name", ["c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c6_swa_ue8m0"])
 def test_whole_token_plan_16_head_groups(name):
-    """The head grouping the binding picks for whole-token calls on the fp8 ring kernel (16 heads per
+    """The head grouping the library picks for whole-token calls on the fp8 ring kernel (16 heads per
     workgroup): same bar against the oracle."""
     w = wl.make_workload(name, seed=4, T=SMALL_T[name])
-    plan = auto_plan_for(w)  # the library's choice on these lengths: whole tokens, 16 heads per workgroup
-    assert plan.whole_tokens == 1 and plan.heads_per_group == 16
+    plan = _whole_plan(w)
+    plan.heads_per_group = 16  # the grouping sda_choose_plan takes for such calls at full size
     _log(f"[whole hb16] {name} T={w.T}")
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"{name} whole tokens, 16 heads per group")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"{name} whole tokens, 16 heads per group")
 
 
 @pytest.mark.parametrize("fmt,xfmt,width,xwidth,H,hb", [
@@ -494,9 +495,9 @@ def test_whole_token_plan_first_tiles(fmt, xfmt, width, xwidth, H, hb):
     plan = _whole_plan(w)
     plan.heads_per_group = hb
     _log(f"[whole first tiles] fmt {fmt}/{xfmt} width {width}/{xwidth} H={H} hb={hb}")
-    o_ref, l_ref = oracle.attention(w, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(w, nthreads=8, with_abs=True)
     out, lse, dec = DeviceWorkload(w).run(plan=plan)
-    compare(out, lse, o_ref, l_ref, what=f"whole first tiles {fmt}/{xfmt} {width}/{xwidth}")
+    compare(out, lse, o_ref, l_ref, o_abs, what=f"whole first tiles {fmt}/{xfmt} {width}/{xwidth}")
 
 
 def test_whole_token_plan_equals_one_token_parts():
@@ -529,9 +530,9 @@ def test_whole_token_plan_request_lengths_and_sinks():
     e.lst.lens = g.lst.lens[r].copy()
     e.xlst.lens = g.xlst.lens[r].copy()
     e.lst.queries_per_len = e.xlst.queries_per_len = 1
-    o_ref, l_ref = oracle.attention(g, nthreads=8)
+    o_ref, l_ref, o_abs = oracle.attention(g, nthreads=8, with_abs=True)
     out_g, lse_g, _ = DeviceWorkload(g).run(plan=_whole_plan(g))
-    compare(out_g, lse_g, o_ref, l_ref, what="whole tokens, request lengths")
+    compare(out_g, lse_g, o_ref, l_ref, o_abs, what="whole tokens, request lengths")
     out_e, lse_e, _ = DeviceWorkload(e).run(plan=_whole_plan(e))
     assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e)
 

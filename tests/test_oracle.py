@@ -401,6 +401,59 @@ def test_sink_closed_form(orc):
     np.testing.assert_allclose(out_s, out * frac[:, :, None], atol=1e-13)
 
 
+# ------------------------------------------------------------------ out_abs (the tolerance scale)
+
+def test_out_abs_bounds_and_closed_forms(orc):
+    """orc_attn_abs: the weighted mean of |v| under the output's own weights. It bounds |out| (triangle
+    inequality), returns |row| for a single valid row, matches a math.fsum brute force, and with two rows
+    is the logistic mix of their magnitudes."""
+    w = _w(30, xfmt=wl.NVFP4_288, sink=True)
+    out, lse, oabs = orc.attention(w, with_abs=True)
+    out2, lse2 = orc.attention(w)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    assert np.all(oabs >= np.abs(out) - 1e-15 * np.abs(out)) and np.all(oabs >= 0)
+    # brute force of token 1 with the sink
+    q = q_f64(w)
+    rows = np.concatenate([decode_rows(c, [s]) for c, s in valid_rows(w, 1)])
+    for h in range(w.H):
+        z = [w.scale * float(np.dot(q[1, h], r)) for r in rows]
+        sk = float(w.sink[h])
+        M = max(z + [sk])
+        ws = [math.exp(zi - M) for zi in z]
+        den = math.fsum(ws + [math.exp(sk - M)])
+        ref = [math.fsum(wi * abs(r[d]) for wi, r in zip(ws, rows)) / den for d in range(w.d_v)]
+        np.testing.assert_allclose(oabs[1, h], ref, rtol=0, atol=1e-12)
+    # a single valid row: its magnitudes
+    w = _w(31, width=8)
+    w.lst.idx[:, :] = -1
+    w.lst.idx[:, 2] = 77
+    w.lst.lens[:] = 8
+    _, _, oabs = orc.attention(w, with_abs=True)
+    k = decode_rows(w.cache, [77])[0]
+    for t in range(w.T):
+        np.testing.assert_allclose(oabs[t], np.broadcast_to(np.abs(k[:512]), oabs[t].shape), rtol=1e-15)
+    # two rows: a |k0| + (1 - a) |k1|
+    w = _w(32, width=4)
+    w.lst.idx[:, :] = -1
+    w.lst.idx[:, 0] = 5
+    w.lst.idx[:, 3] = 150
+    w.lst.lens[:] = 4
+    _, _, oabs = orc.attention(w, with_abs=True)
+    k = decode_rows(w.cache, [5, 150])
+    q = q_f64(w)
+    for t in range(w.T):
+        for h in range(w.H):
+            z1, z2 = (w.scale * (k @ q[t, h]))
+            a = 1.0 / (1.0 + math.exp(z2 - z1))
+            np.testing.assert_allclose(oabs[t, h], a * np.abs(k[0, :512]) + (1 - a) * np.abs(k[1, :512]), atol=1e-12)
+    # empty tokens: zeros
+    w = _w(33, sink=True)
+    w.lst.lens[:] = 0
+    _, _, oabs = orc.attention(w, with_abs=True)
+    assert np.all(oabs == 0)
+
+
 def test_sink_infinities(orc):
     w = _w(11)
     out, lse = orc.attention(w, sink=None)
@@ -614,11 +667,11 @@ def test_v41_with_identity_rotation_is_the_plain_decode_cast(orc):
     w = _w(44, fmt=wl.FP8_UE8M0, xfmt=wl.FP8_UE8M0, sink=True, T=5)
     w.rope = wl.make_rope(np.random.default_rng(1), w.T, num_positions=64)
     w.rope.positions[:] = 64                                   # outside the table
-    codes, sc, lse, out = orc.attention_v41(w)
+    codes, sc, lse, out, _ = orc.attention_v41(w)
     o, l = orc.attention(w)
     assert np.array_equal(out, o) and np.array_equal(lse, l)
     c2, s2 = orc.mxfp8_out(o, w.rope.positions, w.rope.cos_sin)
     assert np.array_equal(codes, c2) and np.array_equal(sc, s2)
     w.rope.positions[:] = 7
-    codes3, _, lse3, _ = orc.attention_v41(w)
+    codes3, _, lse3, _, _ = orc.attention_v41(w)
     assert not np.array_equal(lse3, l)                         # the rotation reaches the scores
