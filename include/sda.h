@@ -220,6 +220,27 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
                            void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                            void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): sda_sparse_decode_attn without a workspace argument. The workspace is
+ * a static device array of SDA_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends; this call allocates nothing. Every call on one GPU shares that GPU's array (no part of it
+ * needs clearing: each call writes what it reads), so calls on one GPU whose streams overlap race and must
+ * be ordered by the caller. A whole-token plan touches no workspace; a split plan needs
+ * sda_noalloc_workspace_bytes(T, H, d_v, plan) <= SDA_SCRATCH_BYTES, else SDA_ERR_WORKSPACE. Other
+ * arguments and errors as sda_sparse_decode_attn. */
+#define SDA_SCRATCH_BYTES (64u << 20)
+
+/* Host only. Scratch bytes sda_sparse_decode_attn_noalloc needs for this plan (0 for a whole-token plan). */
+size_t sda_noalloc_workspace_bytes(int T, int H, int d_v, const sda_plan* plan /*host*/);
+
+int sda_sparse_decode_attn_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk,
+                                   int d_v, const sda_cache* cache /*host*/, const sda_list* list /*host*/,
+                                   const sda_cache* extra_cache /*host, nullable*/,
+                                   const sda_list* extra_list /*host, nullable*/, const float* attn_sink, float scale,
+                                   const sda_plan* plan /*host*/, const int32_t* meta, const int32_t* num_splits,
+                                   void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                                   int64_t lse_stride_t, void* stream);
+
 /* The decode kernel alone (FlashMLA sparse_decode.h: impl->run, before the combine): same arguments
  * and checks as sda_sparse_decode_attn, but meta and num_splits are required (NULL for a whole-token
  * plan, whose tokens are all touched by a single workgroup, token t's partial going to split t) and

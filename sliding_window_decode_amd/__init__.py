@@ -23,7 +23,9 @@ SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_HIP
 EXPORTED_SYMBOLS = ("sda_make_plan", "sda_choose_plan", "sda_workspace_bytes", "sda_get_sched_meta", "sda_get_sched_meta_host",
                     "sda_sparse_decode_attn", "sda_decode_splits", "sda_workspace_lse_offset",
                     "sda_combine_splits", "sda_status_string", "sda_last_error", "sda_record_bytes",
-                    "sda_format_dims", "sda_workspace_bytes_v41", "sda_sparse_decode_attn_v41")
+                    "sda_format_dims", "sda_workspace_bytes_v41", "sda_sparse_decode_attn_v41",
+                    "sda_noalloc_workspace_bytes", "sda_sparse_decode_attn_noalloc")
+SCRATCH_BYTES = 64 << 20  # SDA_SCRATCH_BYTES
 
 
 class SdaError(RuntimeError):
@@ -85,6 +87,12 @@ def lib():
                                              ctypes.POINTER(sda_list), vp, ctypes.c_float, ctypes.POINTER(sda_plan),
                                              vp, vp, vp, sz, vp, i64, i64, vp, i64, vp]
         L.sda_decode_splits.argtypes = L.sda_sparse_decode_attn.argtypes
+        L.sda_sparse_decode_attn_noalloc.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.POINTER(sda_cache),
+                                                     ctypes.POINTER(sda_list), ctypes.POINTER(sda_cache),
+                                                     ctypes.POINTER(sda_list), vp, ctypes.c_float,
+                                                     ctypes.POINTER(sda_plan), vp, vp, vp, i64, i64, vp, i64, vp]
+        L.sda_noalloc_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sda_plan)]
+        L.sda_noalloc_workspace_bytes.restype = sz
         L.sda_workspace_bytes_v41.argtypes = [i32, i32, ctypes.POINTER(sda_plan)]
         L.sda_workspace_bytes_v41.restype = sz
         L.sda_sparse_decode_attn_v41.argtypes = [vp, i64, i64, i32, i32, ctypes.POINTER(sda_cache),
@@ -273,6 +281,25 @@ def decode_splits(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache], 
     out=None every token leaves as a partial, as in the V4.1 call)."""
     _decode_call(lib().sda_decode_splits, q, cache, lst, extra_cache, extra_lst, attn_sink, scale, plan, meta,
                  num_splits, workspace, out, lse, stream)
+
+
+def sparse_decode_attn_noalloc(q, cache: Cache, lst: SlotList, extra_cache: Optional[Cache],
+                               extra_lst: Optional[SlotList], attn_sink, scale: float, plan: sda_plan, meta,
+                               num_splits, out, lse, stream=None):
+    """The whole op with the library's static scratch as its workspace (no workspace argument)."""
+    T, H, d_qk = q.shape
+    cc, cl = cache.c(), lst.c()
+    xc = extra_cache.c() if extra_cache is not None else None
+    xl = extra_lst.c() if extra_lst is not None else None
+    _check(lib().sda_sparse_decode_attn_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), T, H, d_qk, out.shape[-1], ctypes.byref(cc), ctypes.byref(cl),
+        ctypes.byref(xc) if xc is not None else None, ctypes.byref(xl) if xl is not None else None,
+        _ptr(attn_sink), ctypes.c_float(scale), ctypes.byref(plan), _ptr(meta), _ptr(num_splits),
+        _ptr(out), out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)))
+
+
+def noalloc_workspace_bytes(T: int, H: int, d_v: int, plan: sda_plan) -> int:
+    return int(lib().sda_noalloc_workspace_bytes(T, H, d_v, ctypes.byref(plan)))
 
 
 def workspace_bytes_v41(T: int, H: int, plan: sda_plan) -> int:

@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sda_internal.h"
 
 namespace {
@@ -181,6 +183,37 @@ sda::SchedParams sched_params(int T, const sda_list* list, const sda_list* extra
   s.meta = meta;
   s.num_splits = num_splits;
   return s;
+}
+
+}  // namespace
+
+namespace {
+
+// Workspace of sda_sparse_decode_attn_noalloc: one copy per GPU, held until the process ends. Host code
+// never uses this name as an address: each device's copy is reached through the address that
+// hipGetSymbolAddress returns for it, with that device current.
+static __device__ __align__(256) char scratch[SDA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on the first call on that device.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SDA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(SDA_ERR_HIP, "scratch symbol address missing or misaligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDA_OK;
 }
 
 }  // namespace
@@ -386,7 +419,8 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
                       const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
                       const sda_list* extra_list, const sda_plan* plan, const int32_t* meta, const int32_t* num_splits,
                       void* workspace, size_t workspace_bytes, void* out, int64_t out_stride_t, int64_t out_stride_h,
-                      float* lse, int64_t lse_stride_t, bool no_out = false, bool v41 = false) {
+                      float* lse, int64_t lse_stride_t, bool no_out = false, bool v41 = false,
+                      bool noalloc = false) {
   // no_out: no bf16 output and an optional lse (V4.1 calls, whose fp8 output is checked by the caller, and
   // decode-only calls that leave every token as a partial)
   if (!q) return fail(SDA_ERR_INVALID_ARG, "q is required");
@@ -416,7 +450,11 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
     return fail(SDA_ERR_INVALID_ARG, "a whole-token plan reads no meta or num_splits: pass NULL for both");
   const WorkspaceLayout wl = layout_of(T, H, d_v, plan->num_parts);
   if (!workspace || !aligned(workspace, 256)) return fail(SDA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < (v41 ? wl.total_v41 : wl.total))
+  // noalloc: the static scratch, checked against what the call touches (nothing for a whole-token plan)
+  const size_t need = noalloc ? (plan->whole_tokens ? 0 : wl.total) : (v41 ? wl.total_v41 : wl.total);
+  if (noalloc && workspace_bytes < need)
+    return fail(SDA_ERR_WORKSPACE, "the plan's workspace exceeds SDA_SCRATCH_BYTES");
+  if (workspace_bytes < need)
     return fail(SDA_ERR_WORKSPACE, v41 ? "workspace smaller than sda_workspace_bytes_v41()"
                                        : "workspace smaller than sda_workspace_bytes()");
   return SDA_OK;
@@ -524,15 +562,20 @@ int sda_decode_splits(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
   return SDA_OK;
 }
 
-int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
-                           const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
-                           const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
-                           const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
-                           void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole op; noalloc: the workspace is the static scratch (checked against what the plan touches).
+int decode_attn_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                     const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                     const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                     const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                     void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                     void* stream, bool noalloc) {
   int rc = check_decode_args(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, plan,
                              meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h, lse,
-                             lse_stride_t);
+                             lse_stride_t, false, false, noalloc);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -556,6 +599,47 @@ int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h
                           st);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return SDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
+                           const sda_cache* cache, const sda_list* list, const sda_cache* extra_cache,
+                           const sda_list* extra_list, const float* attn_sink, float scale, const sda_plan* plan,
+                           const int32_t* meta, const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                           void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                           void* stream) {
+  return decode_attn_impl(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, attn_sink,
+                          scale, plan, meta, num_splits, workspace, workspace_bytes, out, out_stride_t, out_stride_h,
+                          lse, lse_stride_t, stream, false);
+}
+
+size_t sda_noalloc_workspace_bytes(int T, int H, int d_v, const sda_plan* plan) {
+  if (!plan || T < 1 || H < 1 || d_v < 1 || plan->num_parts < 1) return 0;
+  // a whole-token plain call writes every token whole: no partials, no schedule
+  return plan->whole_tokens ? 0 : layout_of(T, H, d_v, plan->num_parts).total;
+}
+
+int sda_sparse_decode_attn_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk,
+                                   int d_v, const sda_cache* cache, const sda_list* list,
+                                   const sda_cache* extra_cache, const sda_list* extra_list, const float* attn_sink,
+                                   float scale, const sda_plan* plan, const int32_t* meta, const int32_t* num_splits,
+                                   void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                                   int64_t lse_stride_t, void* stream) {
+  if (!plan) return fail(SDA_ERR_INVALID_ARG, "plan is NULL");
+  if (T < 1 || H < 1 || d_v < 1 || plan->num_parts < 1) return fail(SDA_ERR_INVALID_ARG, "T, H, d_v and num_parts must be >= 1");
+  const size_t need = sda_noalloc_workspace_bytes(T, H, d_v, plan);
+  if (need > (size_t)SDA_SCRATCH_BYTES)
+    return fail(SDA_ERR_WORKSPACE, "the plan's workspace exceeds SDA_SCRATCH_BYTES (use a whole-token plan, fewer "
+                                   "parts or tokens, or sda_sparse_decode_attn with a caller workspace)");
+  void* ws = nullptr;
+  int rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return decode_attn_impl(q, q_stride_t, q_stride_h, T, H, d_qk, d_v, cache, list, extra_cache, extra_list, attn_sink,
+                          scale, plan, meta, num_splits, ws, (size_t)SDA_SCRATCH_BYTES, out, out_stride_t,
+                          out_stride_h, lse, lse_stride_t, stream, true);
 }
 
 int sda_combine_splits(int T, int H, int d_v, const float* o_accum, const float* lse_accum, const int32_t* num_splits,
