@@ -49,8 +49,9 @@ constexpr int kWaves = 8;
 constexpr int kRS = 656;                            // ring row stride: the record (41 chunks of 16 bytes)
 constexpr int kRSC = kRS / 16;
 constexpr int kNB = 2;                              // ring buffers
-constexpr int kRW = kTileRows / kWaves;             // rows gathered by each wave (8)
-constexpr int kNI = (kRW * kRSC + 63) / 64;         // gather instructions per wave and tile (6)
+constexpr int kGW = 4;                              // gathering waves (0 .. 3)
+constexpr int kRW = kTileRows / kGW;                // rows gathered by each gathering wave (16)
+constexpr int kNI = (kRW * kRSC + 63) / 64;         // gather instructions per gathering wave and tile (11)
 constexpr int kPP = 20;                             // floats per (head, k-step) row of the weights array
 
 struct WideSmem {
@@ -59,14 +60,14 @@ struct WideSmem {
   f32x4 sx[2][2][2][4][64];
   // softmax weights in the PV operand layout: [head block][k-step][head][8 hf + e] (16 of kPP used)
   __attribute__((aligned(16))) float pw[2][4][32][kPP];
-  // each row's four fp32 scales: [buffer][gathering wave][scale group][row % 8]
-  __attribute__((aligned(16))) float stab[kNB][kWaves][4][kRW];
+  // each row's four fp32 scales: [buffer][gathering wave][scale group][row % 16]
+  __attribute__((aligned(16))) float stab[kNB][kGW][4][kRW];
   // each row's additive score mask: 0 for a valid row, -inf for a masked one
   __attribute__((aligned(16))) float mtab[kNB][kTileRows];
   float alpha[64];      // per head: factor the running output is rescaled by in this tile
   float hinv[64];       // per head: factor the token's output is multiplied by in its epilogue
-  uint32_t vmask[kNB][kWaves];
-  uint64_t raddr[kWaves][kRW];
+  uint32_t vmask[kNB][kGW];
+  uint64_t raddr[kGW][kRW];
 };
 
 // DPP lane exchanges within groups of eight consecutive lanes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror)
@@ -83,6 +84,29 @@ __device__ __forceinline__ float sum_of_8(float v) {
   v += dpp_f<0xB1>(v);
   v += dpp_f<0x4E>(v);
   return v + dpp_f<0x141>(v);
+}
+
+// fp32 values split into NTERM bf16 terms whose sum reproduces them (exactly for NTERM = 3), converting two
+// values per instruction (v_cvt_pk_bf16_f32, round to nearest even)
+template <int NTERM>
+__device__ __forceinline__ void split_pairs(const float (&v)[8], bf16x8 (&A)[NTERM]) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = v[e];
+#pragma unroll
+  for (int k = 0; k < NTERM; ++k) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 h = bf16x2{(__bf16)r[e], (__bf16)r[e + 1]};
+      A[k][e] = h[0];
+      A[k][e + 1] = h[1];
+      if (k + 1 < NTERM) {
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        r[e] -= __builtin_bit_cast(float, hb << 16);
+        r[e + 1] -= __builtin_bit_cast(float, hb & 0xFFFF0000u);
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -113,7 +137,7 @@ void decode_wide_kernel(DecodeParams p) {
     const int tb = blockIdx.x < (unsigned)p.T ? (int)blockIdx.x : 0;
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-      const int pos = kTileRows * j + kRW * w + lane % kRW;
+      const int pos = kTileRows * j + kRW * (w & 3) + lane % kRW;
       sid_spec[j] = l0.idx[(int64_t)tb * l0.row_stride + (pos < l0.width ? pos : l0.width - 1)];
     }
   }
@@ -129,16 +153,20 @@ void decode_wide_kernel(DecodeParams p) {
   auto load_sid = [&](const Item& it) -> int {
     int sid = -1;
     if (!it.end()) {
-      const int pos = it.pos0 + kRW * w + lane % kRW;
+      const int pos = it.pos0 + kRW * w + lane % kRW;  // gathering waves only
       const ListDev& ld = LD(it.L);
       if (pos < it.n) sid = ld.idx[(int64_t)it.t * ld.row_stride + pos];
     }
     return sid;
   };
   const uint64_t zero_rec = (uint64_t)(const void*)g_zero_record_wide;
-  // Issues the gather of this wave's 8 rows of item `it` into ring buffer b (6 global -> LDS loads of 16
-  // bytes a lane, one of 4 bytes for the scale table) and writes their masks; returns the valid-row mask.
-  auto gather = [&](const Item& it, int sid, int b) -> uint32_t {
+  // The gather of a tile's records is issued by waves 0 .. 3 alone, 16 rows each: the address unit takes
+  // the loads in turn, and while those waves wait to issue, waves 4 .. 7 (which share their SIMDs) run
+  // their QK^T. gather_rows turns this wave's slot ids into record addresses (held in LDS) and the rows'
+  // masks and returns the valid-row mask; gather_issue(i, b) then issues load i: i < kNI a global -> LDS
+  // load of 16 bytes a lane into ring buffer b, i = kNI one of 4 bytes a lane of the records' scales into
+  // the table.
+  auto gather_rows = [&](const Item& it, int sid, int b) -> uint32_t {
     const ListDev& ld = LD(it.L);
     const bool ok = sid >= 0 && sid < ld.slots;
     uint64_t ra = zero_rec;
@@ -147,30 +175,24 @@ void decode_wide_kernel(DecodeParams p) {
       const uint32_t off = (uint32_t)sid & ((1u << ld.page_shift) - 1u);
       ra = (uint64_t)ld.base + (uint64_t)pg_ * (uint64_t)ld.page_stride + (uint64_t)off * (uint64_t)kRS;
     }
-    const uint32_t vm = (uint32_t)__ballot(ok) & 0xFFu;
     if (lane < kRW) {
       sm.raddr[w][lane] = ra;  // read back by the same wave only
       sm.mtab[b][kRW * w + lane] = ok ? 0.0f : kNegInf;
     }
-    char* dst = sm.ring[b] + kRW * w * kRS;
-    uint64_t src[kNI];
-    // the lane's chunk positions are recomputed at every gather (an opaque zero keeps the compiler from
-    // holding them, 19 registers, across the loop)
+    return (uint32_t)__ballot(ok) & 0xFFFFu;
+  };
+  auto gather_issue = [&](int i, int b) {
+    // the lane's chunk position is recomputed at each load (an opaque zero keeps the compiler from holding
+    // the positions of every load across the loop)
     const int lz = lane + opaque_lane_zero();
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
+    if (i < kNI) {
       const int c = 64 * i + lz;
       const int rl = c / kRSC, ch = c - rl * kRSC;
-      src[i] = sm.raddr[w][rl % kRW] + 16 * ch;
+      const uint64_t src = sm.raddr[w][rl % kRW] + 16 * ch;
+      if (i < kNI - 1 || 64 * i + lane < kRW * kRSC) dma16(src, sm.ring[b] + kRW * w * kRS + 1024 * i);
+    } else {  // lane l: scale group l / 16 of row l % 16
+      dma4(sm.raddr[w][lz & 15] + 512 + 4 * ((lz >> 4) & 3), &sm.stab[b][w][0][0]);
     }
-    // lane l < 32: scale group l / 8 of row l % 8
-    const uint64_t ssrc = sm.raddr[w][lz & 7] + 512 + 4 * ((lz >> 3) & 3);
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      if (i < kNI - 1 || 64 * i + lane < kRW * kRSC) dma16(src[i], dst + 1024 * i);
-    }
-    if (lane < 32) dma4(ssrc, &sm.stab[b][w][0][0]);
-    return vm;
   };
 
   // ---- prologue: items k = 0 .. 2, the gather of tile 0 in flight, the slot ids of tile 1
@@ -180,8 +202,8 @@ void decode_wide_kernel(DecodeParams p) {
   Item its[kNB + 1];  // its[j] = tile k + j
 #pragma unroll
   for (int j = 0; j <= kNB; ++j) its[j] = gen_next<kTileRows>(gen, p, tinfo);
-  int sid_next;
-  {
+  int sid_next = -1;
+  if (w < kGW) {
     int sids[kNB];
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
@@ -190,8 +212,10 @@ void decode_wide_kernel(DecodeParams p) {
       else
         sids[j] = load_sid(its[j]);
     }
-    const uint32_t vm = gather(its[0], sids[0], 0);
+    const uint32_t vm = gather_rows(its[0], sids[0], 0);
     if (lane == 0) sm.vmask[0][w] = vm;
+#pragma unroll
+    for (int i = 0; i <= kNI; ++i) gather_issue(i, 0);
     sid_next = sids[1];
   }
 
@@ -236,20 +260,27 @@ void decode_wide_kernel(DecodeParams p) {
     vm_wait<0>();   // tile k's gather (issued one iteration earlier) and everything before it landed
     barrier_lds();  // every wave's gather of tile k landed; ring buffer b ^ 1 is free
 
-    // slot ids of tile k+2, then the gather of tile k+1 into the free buffer
-    const int sid_new = load_sid(its[2]);
-    if (!its[1].end()) {
-      const uint32_t vm = gather(its[1], sid_next, b ^ 1);
+    // slot ids of tile k+2, then the gather of tile k+1 into the free buffer (its loads issued below)
+    const bool gwave = w < kGW;
+    const int sid_new = gwave ? load_sid(its[2]) : -1;
+    const bool gath = gwave && !its[1].end();
+    if (gath) {
+      const uint32_t vm = gather_rows(its[1], sid_next, b ^ 1);
       if (lane == 0) sm.vmask[b ^ 1][w] = vm;
     }
     sid_next = sid_new;
+    auto issue = [&](int i) {
+      if (gath) gather_issue(i, b ^ 1);
+    };
+#pragma unroll
+    for (int i = 0; i <= kNI; ++i) issue(i);
 
     const Item it0 = its[0], it1 = its[1];
     const bool last = it1.end() || it1.t != it0.t;  // tile k is the token's last in this part
     const char* ring = sm.ring[b];
     uint32_t vany = 0;
 #pragma unroll
-    for (int j = 0; j < kWaves; ++j) vany |= sm.vmask[b][j];
+    for (int j = 0; j < kGW; ++j) vany |= sm.vmask[b][j];
 
     // ---- QK^T: partial scores of this wave's head block, row block and dims half
     if (vany) {
@@ -276,11 +307,11 @@ void decode_wide_kernel(DecodeParams p) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qf[gi][s2][0], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qf[gi][s2][1], acc, 0, 0, 0);
         }
-        // fold the rows' scales of group g: lane rows 32 qrb + 8 a + 4 hf + 0..3 (gathered by wave 4 qrb + a,
-        // its rows 4 hf + 0..3)
+        // fold the rows' scales of group g: lane rows 32 qrb + 8 a + 4 hf + 0..3 (gathered by wave
+        // 2 qrb + a / 2, its rows 8 (a % 2) + 4 hf + 0..3)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const f32x4 sc = *(const f32x4*)&sm.stab[b][4 * qrb + a][g][4 * hf];
+          const f32x4 sc = *(const f32x4*)&sm.stab[b][2 * qrb + (a >> 1)][g][8 * (a & 1) + 4 * hf];
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[4 * a + e] = __builtin_fmaf(acc[4 * a + e], sc[e], S[4 * a + e]);
         }
@@ -395,11 +426,11 @@ void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) x[db] = lds_tr8(vbase + 16 * kk * kRS + 32 * db);
         // P' = p x the rows' scale of group pg, split into bf16 terms (rows 16 kk + 8 c + 4 hf + 0..3 were
-        // gathered by wave 2 kk + c, its rows 4 hf + 0..3)
+        // gathered by wave kk, its rows 8 c + 4 hf + 0..3)
         bf16x8 A[NTERM];
         {
-          const f32x4 s0 = *(const f32x4*)&sm.stab[b][2 * kk][pg][4 * hf];
-          const f32x4 s1 = *(const f32x4*)&sm.stab[b][2 * kk + 1][pg][4 * hf];
+          const f32x4 s0 = *(const f32x4*)&sm.stab[b][kk][pg][4 * hf];
+          const f32x4 s1 = *(const f32x4*)&sm.stab[b][kk][pg][8 + 4 * hf];
           const f32x4 p0 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf];
           const f32x4 p1 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf + 4];
           float pg8[8];
@@ -408,7 +439,7 @@ void decode_wide_kernel(DecodeParams p) {
             pg8[e] = p0[e] * s0[e];
             pg8[4 + e] = p1[e] * s1[e];
           }
-          split_terms<NTERM>(pg8, A);
+          split_pairs<NTERM>(pg8, A);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 #pragma unroll
