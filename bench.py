@@ -453,11 +453,14 @@ def main():
         wc = w if (name == args.workload and args.seed == 0) else wl.make_workload(name, seed=0)
         dwc = dw if wc is w else DeviceWorkload(wc)
         pc = plan_for(wc)
+        if args.precision is not None:
+            pc.precision = args.precision
         res, _ = measure(wc, dwc, pc, args.steps, args.warmup)
         entry = {"heads": wc.H, "tokens": wc.T, **res}
         if name == HEADLINE and pc.whole_tokens:
             # the plan the configuration names: split-KV sized to 256 CUs + combine
             sp = sda.make_plan(wc.T, wc.H, wc.d_qk, wc.lst.width, wc.xlst.width if wc.xlst is not None else 0)
+            sp.precision = pc.precision
             entry["split_plan"], _ = measure(wc, dwc, sp, args.steps, args.warmup)
         per[name] = entry
         log(f"[bench]   {name}: hot {res['hot']['step_us']} us, cold {res['cold']['step_us']} us")

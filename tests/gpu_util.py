@@ -124,6 +124,38 @@ def eps_for(plan) -> float:
     return EPS_P1 if plan is not None and plan.precision == 1 else EPS_FP32
 
 
+def error_stats(out_gpu, lse_gpu, o_ref, l_ref, o_abs, tokens=None, eps=EPS_FP32):
+    """The error figures compare() asserts on, without asserting: max-abs and rel-L2 against the RNE-bf16 oracle,
+    the LSE error, the elements beyond 1e-2 (midpoint roundings) and those of them outside the eps window."""
+    got = out_gpu.float().cpu().numpy().astype(np.float64)
+    lg = lse_gpu.float().cpu().numpy().astype(np.float64)
+    if tokens is not None:
+        got, lg = got[tokens], lg[tokens]
+    import oracle  # test infrastructure: imported here, so that bench.py's timed path never loads it
+
+    ref = oracle.bf16_rne(o_ref)
+    diff = np.abs(got - ref)
+    nrm = float(np.linalg.norm(ref))
+    inf_ref = ~np.isfinite(l_ref)
+    o_abs = np.asarray(o_abs, dtype=np.float64)
+    assert o_abs.shape == o_ref.shape, f"out_abs shape {o_abs.shape} against {o_ref.shape}"
+    over = diff > OUT_MAX_ABS
+    # the bf16 values that round some y with |y - x| <= eps o_abs (rounding is monotonic: all between these two)
+    lo = oracle.bf16_rne(o_ref - eps * o_abs)
+    hi = oracle.bf16_rne(o_ref + eps * o_abs)
+    bad = over & ~((got >= lo) & (got <= hi))
+    st = dict(max_abs=float(diff.max()) if diff.size else 0.0,
+              rel_l2=float(np.linalg.norm(got - ref) / nrm) if nrm > 0 else float(np.linalg.norm(got)),
+              lse_max_abs=float(np.abs(lg[~inf_ref] - l_ref[~inf_ref]).max()) if (~inf_ref).any() else 0.0,
+              midpoint_roundings=int(over.sum()), n=int(diff.size), eps=eps, n_bad=int(bad.sum()),
+              finite=bool(np.all(np.isfinite(got))),
+              lse_inf_match=bool(np.array_equal(inf_ref, ~np.isfinite(lg)) and np.array_equal(l_ref[inf_ref], lg[inf_ref])))
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:4]
+        st["first_bad"] = [(int(k), float(o_ref.ravel()[k]), float(o_abs.ravel()[k]), float(got.ravel()[k])) for k in i]
+    return st
+
+
 def compare(out_gpu, lse_gpu, o_ref, l_ref, o_abs, tokens=None, what="", eps=EPS_FP32):
     """Assert the tolerances element by element; returns a dict of the error figures.
 
@@ -133,37 +165,10 @@ def compare(out_gpu, lse_gpu, o_ref, l_ref, o_abs, tokens=None, what="", eps=EPS
     either neighbour is a correct rounding of a result that precise, and where |x| >= 2 one bf16 ulp (2^-6
     and up) exceeds 1e-2 by itself. No count of such elements is allowed for; each is checked on its own.
     rel-L2 <= 5e-3 over all elements. lse: within 1e-3 absolute, infinities exact (with their signs)."""
-    got = out_gpu.float().cpu().numpy().astype(np.float64)
-    lg = lse_gpu.float().cpu().numpy().astype(np.float64)
-    if tokens is not None:
-        got, lg = got[tokens], lg[tokens]
-    import oracle  # test infrastructure: imported here, so that bench.py's timed path never loads it
-
-    ref = oracle.bf16_rne(o_ref)
-    diff = np.abs(got - ref)
-    max_abs = float(diff.max()) if diff.size else 0.0
-    nrm = float(np.linalg.norm(ref))
-    rel_l2 = float(np.linalg.norm(got - ref) / nrm) if nrm > 0 else float(np.linalg.norm(got))
-    inf_ref = ~np.isfinite(l_ref)
-    assert np.array_equal(inf_ref, ~np.isfinite(lg)), f"{what}: LSE infinities differ"
-    assert np.array_equal(l_ref[inf_ref], lg[inf_ref]), f"{what}: LSE infinity signs differ"
-    lse_err = float(np.abs(lg[~inf_ref] - l_ref[~inf_ref]).max()) if (~inf_ref).any() else 0.0
-    over = diff > OUT_MAX_ABS
-    # the bf16 values that round some y with |y - x| <= eps |x| (rounding is monotonic: all between these two)
-    o_abs = np.asarray(o_abs, dtype=np.float64)
-    assert o_abs.shape == o_ref.shape, f"{what}: out_abs shape {o_abs.shape} against {o_ref.shape}"
-    lo = oracle.bf16_rne(o_ref - eps * o_abs)
-    hi = oracle.bf16_rne(o_ref + eps * o_abs)
-    in_window = (got >= lo) & (got <= hi)
-    bad = over & ~in_window
-    info = dict(max_abs=max_abs, rel_l2=rel_l2, lse_max_abs=lse_err, midpoint_roundings=int(over.sum()),
-                n=int(diff.size), eps=eps)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    if bad.any():
-        i = np.flatnonzero(bad.ravel())[:4]
-        info["first_bad"] = [(int(k), float(o_ref.ravel()[k]), float(got.ravel()[k])) for k in i]
-        info["n_bad"] = int(bad.sum())
-    assert not bad.any(), f"{what}: elements beyond 1e-2 and outside the rounding window {info}"
-    assert rel_l2 <= OUT_REL_L2, f"{what}: out rel-L2 {rel_l2:.3e} {info}"
-    assert lse_err <= LSE_MAX_ABS, f"{what}: lse max-abs {lse_err:.3e} {info}"
+    info = error_stats(out_gpu, lse_gpu, o_ref, l_ref, o_abs, tokens, eps)
+    assert info["lse_inf_match"], f"{what}: LSE infinities differ {info}"
+    assert info["finite"], f"{what}: non-finite output"
+    assert info["n_bad"] == 0, f"{what}: elements beyond 1e-2 and outside the rounding window {info}"
+    assert info["rel_l2"] <= OUT_REL_L2, f"{what}: out rel-L2 {info['rel_l2']:.3e} {info}"
+    assert info["lse_max_abs"] <= LSE_MAX_ABS, f"{what}: lse max-abs {info['lse_max_abs']:.3e} {info}"
     return info
