@@ -255,24 +255,7 @@ void decode_ring_kernel(DecodeParams p) {
     const float lt = sum_across_groups(l);
     const int h = h0 + li;
     float inv, lse_out;
-    if (whole) {
-      const float Mx = fmaxf(m, sink2);
-      if (Mx == kNegInf) {
-        inv = 0.f;
-        lse_out = kNegInf;
-      } else if (sink2 == kPosInf) {
-        inv = 0.f;
-        lse_out = kPosInf;
-      } else {
-        const float fo = (m == kNegInf) ? 0.f : fast_exp2(m - Mx);
-        const float den = lt * fo + (sink2 != kNegInf ? fast_exp2(sink2 - Mx) : 0.f);
-        inv = den > 0.f ? fo / den : 0.f;
-        lse_out = den > 0.f ? (Mx + __log2f(den)) * kLn2 : kNegInf;
-      }
-    } else {
-      inv = lt > 0.f ? 1.0f / lt : 0.f;
-      lse_out = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
-    }
+    token_output_factor(m, lt, sink2, whole, inv, lse_out);
     float ir[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * G + r);
@@ -453,15 +436,15 @@ void decode_ring_kernel(DecodeParams p) {
           for (int dg = 0; dg < NDG; ++dg) {  // the group's two 64-dim scales (the bf16 dims: 1)
             const int gi = NDG * sub + dg;
             const uint32_t wd = *(const uint16_t*)(ring + lane * RS + 584 + 2 * gi);
-            sm.vs[2 * gi][lane] = ue8m0_scale(wd);
-            sm.vs[2 * gi + 1][lane] = gi == 3 ? 1.0f : ue8m0_scale(wd >> 8);
+            sm.vs[2 * gi][lane] = ue8m0_value(wd);
+            sm.vs[2 * gi + 1][lane] = gi == 3 ? 1.0f : ue8m0_value(wd >> 8);
           }
         } else if constexpr (kUe8m0) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
             const uint32_t wd = *(const uint32_t*)(ring + vs_off + 4 * dg);  // the group's 4 ue8m0 bytes
 #pragma unroll
-            for (int sg = 0; sg < 4; ++sg) sm.vs[4 * (NDG * sub + dg) + sg][lane] = ue8m0_scale(wd >> (8 * sg));
+            for (int sg = 0; sg < 4; ++sg) sm.vs[4 * (NDG * sub + dg) + sg][lane] = ue8m0_value(wd >> (8 * sg));
           }
         } else {
 #pragma unroll
@@ -508,12 +491,13 @@ void decode_ring_kernel(DecodeParams p) {
         const bool bump = tmax > m + 8.0f;
         const float m_new = bump ? tmax : m;
         const float alpha = bump ? fast_exp2(m - m_new) : 1.0f;
+        const float mref = m_new == kNegInf ? 0.f : m_new;  // all rows masked so far: exp2(-inf) = 0
         float ps = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pv[kk][e] = (m_new == kNegInf) ? 0.f : fast_exp2(z[kk][e] - m_new);
+            pv[kk][e] = fast_exp2(z[kk][e] - mref);
             ps += pv[kk][e];
           }
         }

@@ -211,6 +211,11 @@ void decode_kernel(DecodeParams p) {
         e4m3x4_to_bf16_scaled(x[1], cs, y[2], y[3]);
         e4m3x4_to_bf16_scaled(x[2], cs, y[4], y[5]);
         e4m3x4_to_bf16_scaled(x[3], cs, y[6], y[7]);
+        if (ue8m0 || m1) {  // scale byte 255 is NaN in the MX encoding: the group's values are NaN
+          const bool nan_scale = (__builtin_bit_cast(uint32_t, cs) >> 23) == 255u;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = nan_scale ? 0x7FC07FC0u : y[i];
+        }
         const int f = ((r & 3) << 1) | ((r >> 2) & 1);
         char* row = sm.tile + r * RS;
         const int c0 = 2 * c, c1 = 2 * c + 1;
@@ -355,10 +360,11 @@ void decode_kernel(DecodeParams p) {
         const bool bump = tmax > m[hb] + 8.0f;
         const float m_new = bump ? tmax : m[hb];
         const float alpha = bump ? fast_exp2(m[hb] - m_new) : 1.0f;
+        const float mref = m_new == kNegInf ? 0.f : m_new;  // all rows masked so far: exp2(-inf) = 0
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[hb][e] = (m_new == kNegInf) ? 0.f : fast_exp2(z[e] - m_new);
+          pv[hb][e] = fast_exp2(z[e] - mref);
           ps += pv[hb][e];
         }
         l[hb] = l[hb] * alpha + ps;
@@ -413,26 +419,7 @@ void decode_kernel(DecodeParams p) {
         const float lt = sum_across_groups(l[hb]);
         const int h = h0 + 16 * hb + li;
         float inv, lse_out;
-        if (whole) {
-          const bool has_sink = p.sink != nullptr;
-          const float s2 = has_sink ? p.sink[h] * kLog2e : kNegInf;
-          const float Mx = fmaxf(m[hb], s2);
-          if (Mx == kNegInf) {
-            inv = 0.f;
-            lse_out = kNegInf;
-          } else if (s2 == kPosInf) {
-            inv = 0.f;
-            lse_out = kPosInf;
-          } else {
-            const float fo = (m[hb] == kNegInf) ? 0.f : fast_exp2(m[hb] - Mx);
-            const float den = lt * fo + (has_sink ? fast_exp2(s2 - Mx) : 0.f);
-            inv = den > 0.f ? fo / den : 0.f;
-            lse_out = den > 0.f ? (Mx + __log2f(den)) * kLn2 : kNegInf;
-          }
-        } else {
-          inv = lt > 0.f ? 1.0f / lt : 0.f;
-          lse_out = lt > 0.f ? (m[hb] + __log2f(lt)) * kLn2 : kNegInf;
-        }
+        token_output_factor(m[hb], lt, p.sink != nullptr ? p.sink[h] * kLog2e : kNegInf, whole, inv, lse_out);
         float ir[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * G + r);

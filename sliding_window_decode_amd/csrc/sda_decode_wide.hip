@@ -370,24 +370,7 @@ void decode_wide_kernel(DecodeParams p) {
       const bool whole = it0.whole && !p.all_partial;
       const float lt = sum_of_8(l);
       float inv, lse_out;
-      if (whole) {
-        const float Mx = fmaxf(m, sink2);
-        if (Mx == kNegInf) {
-          inv = 0.f;
-          lse_out = kNegInf;
-        } else if (sink2 == kPosInf) {
-          inv = 0.f;
-          lse_out = kPosInf;
-        } else {
-          const float fo = (m == kNegInf) ? 0.f : fast_exp2(m - Mx);
-          const float den = lt * fo + (sink2 != kNegInf ? fast_exp2(sink2 - Mx) : 0.f);
-          inv = den > 0.f ? fo / den : 0.f;
-          lse_out = den > 0.f ? (Mx + __log2f(den)) * kLn2 : kNegInf;
-        }
-      } else {
-        inv = lt > 0.f ? 1.0f / lt : 0.f;
-        lse_out = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
-      }
+      token_output_factor(m, lt, sink2, whole, inv, lse_out);
       if (sq == 0) {
         const int h = h0 + 8 * w + h8;
         sm.hinv[8 * w + h8] = inv;

@@ -42,9 +42,18 @@ __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_
 }
 
 // The same with a power-of-two scale applied by the conversion: the scale operand contributes only
-// its exponent, so passing the float with exponent field e (and no mantissa) multiplies by 2^(e - 127)
-// -- an ue8m0 scale byte e used as it is. Exact while the products stay within the bf16 range.
+// its exponent field, read as an OCP MX E8M0 byte, so passing the float whose exponent field is an ue8m0
+// scale byte e multiplies by 2^(e - 127), 2^-127 for e = 0 and NaN for e = 255. Exact while the products
+// stay within the bf16 range. Only for the conversions' scale operand: as an fp32 value the same bits are
+// 0 for e = 0 and +inf for e = 255 (ue8m0_value gives the value).
 __device__ __forceinline__ float ue8m0_scale(uint32_t byte) { return __builtin_bit_cast(float, (byte & 0xFFu) << 23); }
+
+// The value of an ue8m0 scale byte as an fp32 multiplier: 2^(e - 127), with the fp32 denormal 2^-127 for
+// e = 0 and NaN for e = 255 (OCP MX E8M0), the values the scaled conversions take from ue8m0_scale.
+__device__ __forceinline__ float ue8m0_value(uint32_t byte) {
+  const uint32_t b = byte & 0xFFu;
+  return __builtin_bit_cast(float, b == 0u ? 0x00400000u : (b == 255u ? 0x7FC00000u : b << 23));
+}
 __device__ __forceinline__ void e4m3x4_to_bf16_scaled(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
   bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
   bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true);
@@ -86,6 +95,36 @@ __device__ __forceinline__ float max_across_groups(float v) {
 __device__ __forceinline__ float sum_across_groups(float v) {
   v += __shfl_xor(v, 16);
   return v + __shfl_xor(v, 32);
+}
+
+// A (token, head)'s output factor and LSE from its running max m and weight sum lt (base 2, the sum over all
+// its rows) and the sink logit sink2 (log2 units; -inf without a sink), folded in when the token is whole:
+// inv multiplies the accumulated output, lse_out is ln(e^sink + sum e^z) (no rows and no sink: 0 and -inf;
+// an infinite sink: 0 and +inf). For a split (whole = false) they normalize the partial, sink left out.
+// A NaN sum (a row whose scores are NaN, e.g. an ue8m0 scale byte 255) gives a NaN factor and LSE.
+__device__ __forceinline__ void token_output_factor(float m, float lt, float sink2, bool whole, float& inv,
+                                                    float& lse_out) {
+  // lt * 0 is 0, or NaN for a NaN sum; !(x <= 0) holds for x > 0 and for NaN
+  if (whole) {
+    const float Mx = fmaxf(m, sink2);
+    if (Mx == kNegInf) {
+      inv = lt * 0.f;
+      lse_out = lt * 0.f + kNegInf;
+    } else if (sink2 == kPosInf) {
+      inv = 0.f;
+      lse_out = kPosInf;
+    } else {
+      const float fo = (m == kNegInf) ? 0.f : fast_exp2(m - Mx);
+      const float den = lt * fo + (sink2 != kNegInf ? fast_exp2(sink2 - Mx) : 0.f);
+      const bool pos = !(den <= 0.f);
+      inv = pos ? fo / den : 0.f;
+      lse_out = pos ? (Mx + __log2f(den)) * kLn2 : kNegInf;
+    }
+  } else {
+    const bool pos = !(lt <= 0.f);
+    inv = pos ? 1.0f / lt : 0.f;
+    lse_out = pos ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  }
 }
 
 // Split fp32 values into NTERM bf16 terms whose sum reproduces them (exactly for NTERM = 3: each term

@@ -152,6 +152,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
   float M = sk;
   float den = has_sink ? 1.0f : 0.0f;  // exp(sk - M) with M = sk
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bool nan_part = false;  // a partial with a NaN LSE (a NaN in its rows) makes the token NaN
   for (int k0 = 0; k0 < n; k0 += KB) {
     float lk[KB];
     f32x4 v[KB][2];
@@ -166,7 +167,10 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
     float bm = M;
 #pragma unroll
     for (int j = 0; j < KB; ++j)
-      if (k0 + j < n) bm = fmaxf(bm, lk[j]);
+      if (k0 + j < n) {
+        bm = fmaxf(bm, lk[j]);
+        nan_part |= lk[j] != lk[j];
+      }
     if (bm == kNegInf || bm == kPosInf) {
       M = bm;
       continue;
@@ -183,6 +187,10 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
       acc[1] += wj * v[j][1];
     }
     M = bm;
+  }
+  if (nan_part) {
+    M = __builtin_nanf("");
+    den = M;
   }
   const bool ok = !(M == kNegInf || M == kPosInf);
   if constexpr (V41) {

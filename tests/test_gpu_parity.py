@@ -335,6 +335,63 @@ def test_every_e4m3_code_decodes_exactly():
         assert np.array_equal(out[t, 0].float().cpu().numpy(), oracle.bf16_rne(ref[:512]))
 
 
+def _ue8m0_sweep_workload(H, nan_slot=None, width=40):
+    """16 FP8_UE8M0 records whose 16 scale bytes sweep 0..254 ((16 r + g) % 255 for record r, group g), codes of
+    magnitude 1..1.875 (so every value c 2^(e - 127) is a bf16 number, 2^-127 scale included), and token t's
+    list holding record t alone; q = 0, so each output row is its record exactly and every lse is 0.
+    nan_slot: a 17th record with scale byte 255 in group 5, read alone by a 17th token. width: list width (the
+    other entries -1)."""
+    rng = np.random.default_rng(77)
+    n = 17 if nan_slot else 16
+    rec = np.zeros((64, 528), dtype=np.uint8)
+    mags = rng.integers(0x38, 0x40, size=(n, 512)).astype(np.uint8)
+    signs = (rng.integers(0, 2, size=(n, 512)) * 0x80).astype(np.uint8)
+    rec[:n, :512] = mags | signs
+    for r in range(16):
+        rec[r, 512:528] = [(16 * r + g) % 255 for g in range(16)]
+    if nan_slot:
+        rec[16, 512:528] = 127
+        rec[16, 512 + 5] = 255
+    c = wl.Cache(wl.FP8_UE8M0, 1, 64, 64 * 528, rec.reshape(-1).copy())
+    idx = np.full((n, width), -1, dtype=np.int32)
+    idx[np.arange(n), (7 * np.arange(n) + width - 40) % width] = np.arange(n)
+    lst = wl.SlotList(idx, width, np.full(n, width, dtype=np.int32))
+    q = np.zeros((n, H, 512), dtype=np.uint16)
+    return wl.Workload("ue8m0 byte sweep", n, H, 512, 512, q, c, lst, None, None, None, 0.05)
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_every_ue8m0_scale_byte(H):
+    """Every ue8m0 scale byte 0..254 (vLLM swapab_decode_attn, stage_inputs fp8 branch; OCP MX E8M0): a single
+    valid row returns its record exactly, bit for bit with RNE-bf16 of the oracle, 2^-127 for byte 0 included
+    (16 heads: the ring kernel built for the format; 32: the same at two head sets)."""
+    w = _ue8m0_sweep_workload(H)
+    o_ref, l_ref = oracle.attention(w)
+    out, lse, dec = DeviceWorkload(w).run()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.bf16_rne(o_ref)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} elements differ, first {[(tuple(b), got[tuple(b)], ref[tuple(b)]) for b in bad[:4]]}"
+    assert np.array_equal(lse.cpu().numpy(), l_ref.astype(np.float32))
+    # byte 0 of record 0 covers dims 0..31: its values are codes x 2^-127
+    assert np.all(np.abs(ref[0, 0, :32]) < 2.0 ** -126) and np.all(ref[0, 0, :32] != 0)
+
+
+@pytest.mark.parametrize("parts", [None, 68])
+def test_ue8m0_byte_255_gives_nan_rows(parts):
+    """Scale byte 255 is NaN in the MX encoding: the token that reads such a record gets NaN outputs and a NaN
+    LSE, as the oracle does; the other tokens are untouched. parts = 68: lists of 256 entries (4 tiles) on 68
+    parts, so each token is split in four, three partials without a valid row (LSE -inf) and one with the
+    record, and the NaN partial is carried through the combine."""
+    w = _ue8m0_sweep_workload(16, nan_slot=True, width=40 if parts is None else 256)
+    o_ref, l_ref = oracle.attention(w)
+    assert np.all(np.isnan(o_ref[16])) and np.all(np.isnan(l_ref[16]))
+    out, lse, _ = DeviceWorkload(w).run(plan=None if parts is None else sda.sda_plan(parts, 16, 0, 3))
+    got = out.float().cpu().numpy()
+    assert np.all(np.isnan(got[16])) and np.all(np.isnan(lse[16].cpu().numpy()))
+    assert np.array_equal(got[:16].astype(np.float64), oracle.bf16_rne(o_ref[:16]))
+
+
 def test_every_e2m1_code_and_block_scale():
     rng = np.random.default_rng(6)
     c = wl.make_cache(rng, wl.NVFP4_288, 64, page_size=64)
