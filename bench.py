@@ -40,6 +40,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_decode_amd", "csrc", f)
                          "sda_internal.h", "sda_v41.hip")]
 CALIB_BYTES = 256 << 20        # the plain copy that calibrates the HBM byte counters
 COLD_BYTES = 600e6             # rotated buffer sets exceed twice the MALL
+RAMP_S = 0.3                   # untimed steps before the headline's warmup, for the clocks to settle
 HEADLINE = "c5_topk_v32"
 BENCH_CONFIGS = ("c1_tiny_swa", "c2_swa_h128", "c3_swa_fp8extra", "c4_swa_nvfp4extra", "c5_topk_v32")
 BOX_CPU_SHARE = 16             # host CPUs a one-GPU machine allots to a job
@@ -277,6 +278,21 @@ class Runner:
                           for _ in range(nsets)])
         return nsets, per_set
 
+    def ramp(self, seconds):
+        """Untimed steps for about `seconds` of wall time before anything is timed, so that the GPU's clocks and
+        power state have settled (the first tens of milliseconds after an idle period run measurably slower)."""
+        torch = self.torch
+        n = len(self.calls)
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(32):
+                for f in self.calls[i % n][0]:
+                    f()
+                i += 1
+            torch.cuda.synchronize()
+        return i
+
     def time(self, steps, warmup):
         """(mean step, mean decode-kernel duration, host enqueue time per step), all in ms. The step is timed
         over exactly `steps` back-to-back steps between two synchronizations, with HIP events on the launch
@@ -323,6 +339,7 @@ def measure(w, dw, plan, steps, warmup, cold=True):
     and of the decode kernel."""
     byts, flops, rows = algorithmic_work(w)
     r = Runner(w, dw, plan)
+    r.ramp(0.05)
     st_h, k_h, ho_h = r.time(steps, warmup)
     res = {"plan": plan_dict(plan), "alg_bytes": byts, "alg_flops": flops, "valid_rows": rows,
            "hot": {"step_us": round(st_h * 1e3, 2), "kernel_us": round(k_h * 1e3, 2),
@@ -406,6 +423,8 @@ def main():
     if not args.hot:
         nsets, per_set = r.make_cold_sets()
         log(f"[bench] cold: {nsets} buffer sets of {per_set / 1e6:.1f} MB")
+    ramp_steps = r.ramp(RAMP_S)
+    log(f"[bench] clock ramp: {ramp_steps} untimed steps in {RAMP_S:.1f} s")
     ms_step, ms_kern, ms_host = r.time(args.steps, max(args.warmup, len(r.sets)))
     log(f"[bench] step {ms_step * 1e3:.2f} us, decode kernel {ms_kern * 1e3:.2f} us, host enqueue "
         f"{ms_host * 1e3:.2f} us per step")
@@ -422,6 +441,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_steps": ramp_steps,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -9,7 +9,8 @@
 // tile k is computed the records of tiles k+1 .. k+NB-1 are in flight; nothing is staged in registers.
 // Every wave gathers 16 / HS rows; wave (head set hs, block wr), tile k:
 //   gather: its rows of tile k+NB-1 (global_load_lds_dwordx4, lane-contiguous LDS destinations),
-//           after turning their slot ids (loaded one tile earlier) into addresses
+//           after turning their slot ids (loaded one tile earlier) into addresses; issued once the
+//           scores of tile k are in LDS (the address unit's time overlaps softmax and PV)
 //   QK^T:   rows 16wr .. 16wr+15 against the set's heads over all dims, v_mfma_f32_16x16x32_bf16 with
 //           rows on M and heads on N; the fp8 codes are widened to bf16 (exactly) as they are read;
 //           one accumulator per 128-dim scale group, folded with the rows' scales afterwards
@@ -287,8 +288,9 @@ void decode_ring_kernel(DecodeParams p) {
   const uint32_t vs_off = (uint32_t)(lane * RS + 512 + 4 * NDG * sub);      // + 4 dg: scale of group NDG sub + dg
 
   // Global operations this wave certainly issued after each gather, for the wait on that gather: the
-  // Q loads that follow the gather in its iteration (cnt_tail), and everything of each later
-  // iteration (cnt_iter: output stores, the next gather, Q loads). Slot id loads are not counted
+  // Q loads that follow the gather in its iteration (cnt_tail: only in the prologue, as a loop iteration
+  // issues its gather last), and everything of each later iteration (cnt_iter: output stores, Q loads, the
+  // next gather). Slot id loads are not counted
   // (a load whose lanes are all masked may be skipped), nor the slot-scale load of a gather, so the
   // counts are lower bounds and the wait never returns early.
   constexpr int QN = 2 * NQJ + (kRope ? NQR : 0);  // 16-byte Q loads
@@ -317,7 +319,7 @@ void decode_ring_kernel(DecodeParams p) {
       vm_wait_atmost(after < 63 ? after : 63);
     }
     barrier_lds();  // every wave's gather of tile k landed; ring buffer (k-1) % NB is free
-    int c_iter = 0, c_tail = 0;  // this iteration's counts
+    int c_iter = 0;  // this iteration's count
 
     if (ep_t >= 0) {
       epilogue(ep_t, ep_s, ep_n);
@@ -325,14 +327,9 @@ void decode_ring_kernel(DecodeParams p) {
       ep_t = -1;
       c_iter += SN;
     }
-    // slot ids of tile k+NB, then the gather of tile k+NB-1 into the free buffer
+    // slot ids of tile k+NB (the gather of tile k+NB-1 into the free buffer follows the scores barrier)
     const int sid_new = load_sid(its[NB]);
-    if (!its[NB - 1].end()) {
-      const int bg = (k + NB - 1) % NB;
-      const uint32_t vm = gather(its[NB - 1], sid_next, bg);
-      if (lane == 0) sm.vmask[bg][w] = vm;
-      c_iter += NI;
-    }
+    const int sid_g = sid_next;
     sid_next = sid_new;
 
     const Item it0 = its[0], it1 = its[1];
@@ -458,7 +455,14 @@ void decode_ring_kernel(DecodeParams p) {
     if (!it1.end() && it1.t != it0.t) {
       load_q(it1.t);
       c_iter += QN;
-      c_tail = QN;
+    }
+    // the gather of tile k+NB-1 into the free buffer: the last global operation of the iteration, issued
+    // after QK^T so that the address unit's time overlaps softmax and PV
+    if (!its[NB - 1].end()) {
+      const int bg = (k + NB - 1) % NB;
+      const uint32_t vm = gather(its[NB - 1], sid_g, bg);
+      if (lane == 0) sm.vmask[bg][w] = vm;
+      c_iter += NI;
     }
 
     if (any) {
@@ -676,7 +680,7 @@ void decode_ring_kernel(DecodeParams p) {
       cnt_tail[r] = cnt_tail[r + 1];
     }
     cnt_iter[NB - 2] = c_iter;
-    cnt_tail[NB - 2] = c_tail;
+    cnt_tail[NB - 2] = 0;
 #pragma unroll
     for (int j = 0; j < NB; ++j) its[j] = its[j + 1];
     its[NB] = gen_next<kTileRows>(gen, p, tinfo);

@@ -8,7 +8,8 @@
 //   gather  tile k+1's records into the other of two LDS ring buffers (global -> LDS, 16 bytes a lane,
 //           656-byte rows: an odd number of 16-byte chunks), each record's four fp32 scales into a per-row
 //           table and 0 or -inf into a per-row mask; masked rows (slot -1, out of range, past the length)
-//           read a zero record
+//           read a zero record. Waves 0 .. 3 turn the slot ids into addresses at the top of the tile and
+//           issue the loads once the softmax is done, waiting on the address unit while waves 4 .. 7 run PV
 //   QK^T    wave (hb, dh, rb): heads 32 hb .. 32 hb + 31, rows 32 rb .. 32 rb + 31, dims half dh (fp8 dims
 //           256 dh .. +255, rope dims 512 + 32 dh .. +31): S^T = K Q^T with rows on M and heads on N; K's
 //           fp8 codes are widened (exactly) as read, one accumulator per 128-dim scale group folded with
@@ -162,7 +163,7 @@ void decode_wide_kernel(DecodeParams p) {
   const uint64_t zero_rec = (uint64_t)(const void*)g_zero_record_wide;
   // The gather of a tile's records is issued by waves 0 .. 3 alone, 16 rows each: the address unit takes
   // the loads in turn, and while those waves wait to issue, waves 4 .. 7 (which share their SIMDs) run
-  // their QK^T. gather_rows turns this wave's slot ids into record addresses (held in LDS) and the rows'
+  // their PV products. gather_rows turns this wave's slot ids into record addresses (held in LDS) and the rows'
   // masks and returns the valid-row mask; gather_issue(i, b) then issues load i: i < kNI a global -> LDS
   // load of 16 bytes a lane into ring buffer b, i = kNI one of 4 bytes a lane of the records' scales into
   // the table.
@@ -188,10 +189,10 @@ void decode_wide_kernel(DecodeParams p) {
     if (i < kNI) {
       const int c = 64 * i + lz;
       const int rl = c / kRSC, ch = c - rl * kRSC;
-      const uint64_t src = sm.raddr[w][rl % kRW] + 16 * ch;
+      const uint64_t src = lds_read_u64_waited(lds_u32(&sm.raddr[w][rl % kRW])) + 16 * ch;
       if (i < kNI - 1 || 64 * i + lane < kRW * kRSC) dma16(src, sm.ring[b] + kRW * w * kRS + 1024 * i);
     } else {  // lane l: scale group l / 16 of row l % 16
-      dma4(sm.raddr[w][lz & 15] + 512 + 4 * ((lz >> 4) & 3), &sm.stab[b][w][0][0]);
+      dma4(lds_read_u64_waited(lds_u32(&sm.raddr[w][lz & 15])) + 512 + 4 * ((lz >> 4) & 3), &sm.stab[b][w][0][0]);
     }
   };
 
@@ -269,11 +270,6 @@ void decode_wide_kernel(DecodeParams p) {
       if (lane == 0) sm.vmask[b ^ 1][w] = vm;
     }
     sid_next = sid_new;
-    auto issue = [&](int i) {
-      if (gath) gather_issue(i, b ^ 1);
-    };
-#pragma unroll
-    for (int i = 0; i <= kNI; ++i) issue(i);
 
     const Item it0 = its[0], it1 = its[1];
     const bool last = it1.end() || it1.t != it0.t;  // tile k is the token's last in this part
@@ -383,6 +379,14 @@ void decode_wide_kernel(DecodeParams p) {
       l = 0.f;
     }
     barrier_lds();  // weights, rescale factors and output factors visible
+    // The gather loads of tile k+1, issued here rather than with the addresses above: the address unit takes
+    // about as long to accept a tile's loads as a SIMD needs for one wave's PV, so waves 0 .. 3 wait for it
+    // while waves 4 .. 7, which share their SIMDs, run their PV products (issued at the top of the tile
+    // they held waves 0 .. 3 past the QK^T that waves 4 .. 7 finish sooner).
+    if (gath) {
+#pragma unroll
+      for (int i = 0; i <= kNI; ++i) gather_issue(i, b ^ 1);
+    }
 
     // ---- PV over dims 128 pg .. 128 pg + 127 of heads 32 phb .. 32 phb + 31
     {

@@ -175,6 +175,14 @@ __device__ __forceinline__ i32x2 lds_tr8(uint32_t lds_addr) {
   return r;
 }
 
+// An 8-byte LDS read that waits for itself (and every LDS operation before it) in the same statement, so
+// that the compiler can neither hoist it nor hold its result across the code around it.
+__device__ __forceinline__ uint64_t lds_read_u64_waited(uint32_t lds_addr) {
+  uint64_t r;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr) : "memory");
+  return r;
+}
+
 // ds_read_b64_tr_b16 as inline assembly, for the same reason as lds_tr8 and under the same rule.
 __device__ __forceinline__ i32x2 lds_tr16(uint32_t lds_addr) {
   i32x2 r;
