@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sda_device.h"
 #include "sda_internal.h"
 #include "sda_items.h"
@@ -47,29 +49,41 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_record_wide[1024];
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 8;
-constexpr int kRS = 656;                            // ring row stride: the record (41 chunks of 16 bytes)
-constexpr int kRSC = kRS / 16;
+constexpr int kRec = 656;                           // record bytes (41 chunks of 16 bytes)
+constexpr int kNC = kRec / 16;                      // chunks per record
 constexpr int kNB = 2;                              // ring buffers
 constexpr int kGW = 4;                              // gathering waves (0 .. 3)
-constexpr int kRW = kTileRows / kGW;                // rows gathered by each gathering wave (16)
-constexpr int kNI = (kRW * kRSC + 63) / 64;         // gather instructions per gathering wave and tile (11)
+constexpr int kNI = (kNC + kGW - 1) / kGW;          // gather instructions per gathering wave and tile (11)
 constexpr int kPP = 20;                             // floats per (head, k-step) row of the weights array
 
+// Ring buffers are chunk-major: chunk q (bytes 16 q .. 16 q + 15 of the record) of row r sits at byte
+// 1024 q + 16 r. One global -> LDS load then moves chunk q of all 64 rows (lane r: row r, lane-contiguous
+// destinations), its source the lane's record address plus a constant.
+__device__ __forceinline__ uint32_t ring_off(int q, int r) { return (uint32_t)(1024 * q + 16 * r); }
+
 struct WideSmem {
-  char ring[kNB][kTileRows * kRS];
+  char ring[kNB][kNC * 1024];
   // partial scores: [dims half][head block][row block][4-row group a][lane] in the 32x32 accumulator layout
   f32x4 sx[2][2][2][4][64];
   // softmax weights in the PV operand layout: [head block][k-step][head][8 hf + e] (16 of kPP used)
   __attribute__((aligned(16))) float pw[2][4][32][kPP];
-  // each row's four fp32 scales: [buffer][gathering wave][scale group][row % 16]
-  __attribute__((aligned(16))) float stab[kNB][kGW][4][kRW];
+  // each row's four fp32 scales: [buffer][scale group][row]
+  __attribute__((aligned(16))) float stab[kNB][4][kTileRows];
   // each row's additive score mask: 0 for a valid row, -inf for a masked one
   __attribute__((aligned(16))) float mtab[kNB][kTileRows];
   float alpha[64];      // per head: factor the running output is rescaled by in this tile
   float hinv[64];       // per head: factor the token's output is multiplied by in its epilogue
-  uint32_t vmask[kNB][kGW];
-  uint64_t raddr[kGW][kRW];
+  uint32_t vany[kNB];  // whether the tile has a valid row
 };
+
+// f(integral_constant<int, I>) for I = B .. E-1, each I a compile-time constant
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // DPP lane exchanges within groups of eight consecutive lanes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror)
 template <int CTRL>
@@ -138,7 +152,7 @@ void decode_wide_kernel(DecodeParams p) {
     const int tb = blockIdx.x < (unsigned)p.T ? (int)blockIdx.x : 0;
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-      const int pos = kTileRows * j + kRW * (w & 3) + lane % kRW;
+      const int pos = kTileRows * j + lane;
       sid_spec[j] = l0.idx[(int64_t)tb * l0.row_stride + (pos < l0.width ? pos : l0.width - 1)];
     }
   }
@@ -154,46 +168,45 @@ void decode_wide_kernel(DecodeParams p) {
   auto load_sid = [&](const Item& it) -> int {
     int sid = -1;
     if (!it.end()) {
-      const int pos = it.pos0 + kRW * w + lane % kRW;  // gathering waves only
+      const int pos = it.pos0 + lane;  // lane: row of the tile
       const ListDev& ld = LD(it.L);
       if (pos < it.n) sid = ld.idx[(int64_t)it.t * ld.row_stride + pos];
     }
     return sid;
   };
   const uint64_t zero_rec = (uint64_t)(const void*)g_zero_record_wide;
-  // The gather of a tile's records is issued by waves 0 .. 3 alone, 16 rows each: the address unit takes
-  // the loads in turn, and while those waves wait to issue, waves 4 .. 7 (which share their SIMDs) run
-  // their PV products. gather_rows turns this wave's slot ids into record addresses (held in LDS) and the rows'
-  // masks and returns the valid-row mask; gather_issue(i, b) then issues load i: i < kNI a global -> LDS
-  // load of 16 bytes a lane into ring buffer b, i = kNI one of 4 bytes a lane of the records' scales into
-  // the table.
-  auto gather_rows = [&](const Item& it, int sid, int b) -> uint32_t {
+  // The gather of a tile's records is issued by waves 0 .. 3 alone, each taking every fourth chunk of all 64
+  // rows: the address unit takes the loads in turn, and while those waves wait to issue, waves 4 .. 7 (which
+  // share their SIMDs) run their PV products. gather_rows turns the lane's slot id (row `lane` of the tile)
+  // into its record address (a masked row: the zero record) and, in wave 0, writes the rows' score masks and
+  // whether any row is valid; gather_issue then issues this wave's loads into ring buffer b: chunks
+  // w + 4 i of every row (source: the row's address plus a constant offset) and scale group w of every row.
+  auto gather_rows = [&](const Item& it, int sid, int b) -> uint64_t {
     const ListDev& ld = LD(it.L);
     const bool ok = sid >= 0 && sid < ld.slots;
     uint64_t ra = zero_rec;
     if (ok) {
       const uint32_t pg_ = (uint32_t)sid >> ld.page_shift;
       const uint32_t off = (uint32_t)sid & ((1u << ld.page_shift) - 1u);
-      ra = (uint64_t)ld.base + (uint64_t)pg_ * (uint64_t)ld.page_stride + (uint64_t)off * (uint64_t)kRS;
+      ra = (uint64_t)ld.base + (uint64_t)pg_ * (uint64_t)ld.page_stride + (uint64_t)off * (uint64_t)kRec;
     }
-    if (lane < kRW) {
-      sm.raddr[w][lane] = ra;  // read back by the same wave only
-      sm.mtab[b][kRW * w + lane] = ok ? 0.0f : kNegInf;
+    if (w == 0) {
+      sm.mtab[b][lane] = ok ? 0.0f : kNegInf;
+      const uint64_t vm = __ballot(ok);
+      if (lane == 0) sm.vany[b] = vm != 0 ? 1u : 0u;
     }
-    return (uint32_t)__ballot(ok) & 0xFFFFu;
+    return ra;
   };
-  auto gather_issue = [&](int i, int b) {
-    // the lane's chunk position is recomputed at each load (an opaque zero keeps the compiler from holding
-    // the positions of every load across the loop)
-    const int lz = lane + opaque_lane_zero();
-    if (i < kNI) {
-      const int c = 64 * i + lz;
-      const int rl = c / kRSC, ch = c - rl * kRSC;
-      const uint64_t src = lds_read_u64_waited(lds_u32(&sm.raddr[w][rl % kRW])) + 16 * ch;
-      if (i < kNI - 1 || 64 * i + lane < kRW * kRSC) dma16(src, sm.ring[b] + kRW * w * kRS + 1024 * i);
-    } else {  // lane l: scale group l / 16 of row l % 16
-      dma4(lds_read_u64_waited(lds_u32(&sm.raddr[w][lz & 15])) + 512 + 4 * ((lz >> 4) & 3), &sm.stab[b][w][0][0]);
-    }
+  auto gather_issue = [&](uint64_t ra, int b) {
+    const uint64_t src = ra + 16 * w;
+    char* dst = sm.ring[b] + 1024 * w;
+    static_assert(64 * (kNI - 1) < 4096, "offsets fit the load's immediate");
+    static_for<0, kNI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      // the immediate offset moves the LDS destination too: the base given is 64 i below chunk w + 4 i
+      if (w + kGW * i < kNC) dma16_at<64 * i>(src, dst + (1024 * kGW - 64) * i);
+    });
+    dma4(ra + 512 + 4 * w, &sm.stab[b][w][0]);
   };
 
   // ---- prologue: items k = 0 .. 2, the gather of tile 0 in flight, the slot ids of tile 1
@@ -209,14 +222,11 @@ void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
       if (spec && !its[j].end() && its[j].L == 0 && its[j].pos0 == kTileRows * j)
-        sids[j] = kTileRows * j + kRW * w + lane % kRW < its[j].n ? sid_spec[j] : -1;
+        sids[j] = kTileRows * j + lane < its[j].n ? sid_spec[j] : -1;
       else
         sids[j] = load_sid(its[j]);
     }
-    const uint32_t vm = gather_rows(its[0], sids[0], 0);
-    if (lane == 0) sm.vmask[0][w] = vm;
-#pragma unroll
-    for (int i = 0; i <= kNI; ++i) gather_issue(i, 0);
+    gather_issue(gather_rows(its[0], sids[0], 0), 0);
     sid_next = sids[1];
   }
 
@@ -265,30 +275,26 @@ void decode_wide_kernel(DecodeParams p) {
     const bool gwave = w < kGW;
     const int sid_new = gwave ? load_sid(its[2]) : -1;
     const bool gath = gwave && !its[1].end();
-    if (gath) {
-      const uint32_t vm = gather_rows(its[1], sid_next, b ^ 1);
-      if (lane == 0) sm.vmask[b ^ 1][w] = vm;
-    }
+    uint64_t ra_next = 0;
+    if (gath) ra_next = gather_rows(its[1], sid_next, b ^ 1);
     sid_next = sid_new;
 
     const Item it0 = its[0], it1 = its[1];
     const bool last = it1.end() || it1.t != it0.t;  // tile k is the token's last in this part
     const char* ring = sm.ring[b];
-    uint32_t vany = 0;
-#pragma unroll
-    for (int j = 0; j < kGW; ++j) vany |= sm.vmask[b][j];
+    const uint32_t vany = sm.vany[b];
 
     // ---- QK^T: partial scores of this wave's head block, row block and dims half
     if (vany) {
-      const char* rrow = ring + (32 * qrb + n) * kRS;
+      const int qrow = 32 * qrb + n;  // the lane's row
       f32x16 S;
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = 0.f;
       // rope dims: bf16 as stored (no scale)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(rrow + 528 + 64 * qdh + 16 * hf + 32 * r), qr[r],
-                                                    S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ring + ring_off(33 + 4 * qdh + hf + 2 * r, qrow)),
+                                                    qr[r], S, 0, 0, 0);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         const int g = 2 * qdh + gi;
@@ -297,17 +303,16 @@ void decode_wide_kernel(DecodeParams p) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          const u32x4 x = *(const u32x4*)(rrow + 128 * g + 32 * s2 + 16 * hf);
+          const u32x4 x = *(const u32x4*)(ring + ring_off(8 * g + 2 * s2 + hf, qrow));
           bf16x8 lo, hi;
           e4m3x16_to_bf16_scaled(x, 1.0f, lo, hi);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qf[gi][s2][0], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qf[gi][s2][1], acc, 0, 0, 0);
         }
-        // fold the rows' scales of group g: lane rows 32 qrb + 8 a + 4 hf + 0..3 (gathered by wave
-        // 2 qrb + a / 2, its rows 8 (a % 2) + 4 hf + 0..3)
+        // fold the rows' scales of group g: lane rows 32 qrb + 8 a + 4 hf + 0..3
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const f32x4 sc = *(const f32x4*)&sm.stab[b][2 * qrb + (a >> 1)][g][8 * (a & 1) + 4 * hf];
+          const f32x4 sc = *(const f32x4*)&sm.stab[b][g][32 * qrb + 8 * a + 4 * hf];
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[4 * a + e] = __builtin_fmaf(acc[4 * a + e], sc[e], S[4 * a + e]);
         }
@@ -383,10 +388,7 @@ void decode_wide_kernel(DecodeParams p) {
     // about as long to accept a tile's loads as a SIMD needs for one wave's PV, so waves 0 .. 3 wait for it
     // while waves 4 .. 7, which share their SIMDs, run their PV products (issued at the top of the tile
     // they held waves 0 .. 3 past the QK^T that waves 4 .. 7 finish sooner).
-    if (gath) {
-#pragma unroll
-      for (int i = 0; i <= kNI; ++i) gather_issue(i, b ^ 1);
-    }
+    if (gath) gather_issue(ra_next, b ^ 1);
 
     // ---- PV over dims 128 pg .. 128 pg + 127 of heads 32 phb .. 32 phb + 31
     {
@@ -406,18 +408,18 @@ void decode_wide_kernel(DecodeParams p) {
       const int G = lane >> 4, j = lane & 15;
       const int er = j >> 1;
       const uint32_t vrow = (uint32_t)(8 * (er >> 2) + 4 * (G >> 1) + (er & 3));
-      const uint32_t vbase = lds_u32(ring) + vrow * kRS + 128 * pg + 16 * (G & 1) + 8 * (j & 1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      // dims 128 pg + 32 db + 16 (G & 1) + 8 (j & 1) + 0..7: chunk 8 pg + 2 db + (G & 1), bytes 8 (j & 1) ..
+      const uint32_t vbase = lds_u32(ring) + ring_off(8 * pg + (G & 1), vrow) + 8 * (j & 1);
+      static_for<0, 4>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
         i32x2 x[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) x[db] = lds_tr8(vbase + 16 * kk * kRS + 32 * db);
-        // P' = p x the rows' scale of group pg, split into bf16 terms (rows 16 kk + 8 c + 4 hf + 0..3 were
-        // gathered by wave kk, its rows 8 c + 4 hf + 0..3)
+        for (int db = 0; db < 4; ++db) x[db] = lds_tr8(vbase + ring_off(2 * db, 16 * kk));
+        // P' = p x the rows' scale of group pg (rows 16 kk + 8 c + 4 hf + 0..3), split into bf16 terms
         bf16x8 A[NTERM];
         {
-          const f32x4 s0 = *(const f32x4*)&sm.stab[b][kk][pg][4 * hf];
-          const f32x4 s1 = *(const f32x4*)&sm.stab[b][kk][pg][8 + 4 * hf];
+          const f32x4 s0 = *(const f32x4*)&sm.stab[b][pg][16 * kk + 4 * hf];
+          const f32x4 s1 = *(const f32x4*)&sm.stab[b][pg][16 * kk + 8 + 4 * hf];
           const f32x4 p0 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf];
           const f32x4 p1 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf + 4];
           float pg8[8];
@@ -435,8 +437,9 @@ void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
           for (int t = 0; t < NTERM; ++t) O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(V, A[t], O[db], 0, 0, 0);
         }
-      }
+      });
     }
+
 
     if (last) {
       // ---- the token's output rows: head h0 + 32 phb + n, dims 128 pg + 32 db + 8 a + 4 hf + 0..3

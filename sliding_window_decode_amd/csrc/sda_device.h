@@ -157,6 +157,12 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void dma16(uint64_t src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 16, 0, 0);
 }
+// The same with a constant byte offset OFF in the load's immediate. The hardware adds it to both addresses:
+// lane l's 16 bytes come from src + OFF and land at lds_wave_base + OFF + 16 l (probed on gfx950).
+template <int OFF>
+__device__ __forceinline__ void dma16_at(uint64_t src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 16, OFF, 0);
+}
 __device__ __forceinline__ void dma4(uint64_t src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 4, 0, 0);
 }
