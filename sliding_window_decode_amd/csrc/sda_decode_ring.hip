@@ -104,7 +104,7 @@ void decode_ring_kernel(DecodeParams p) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // w: wave-uniform (scalar)
   const int hs = w / Shape::WPS, sub = w % Shape::WPS;  // head set; its rows (QK^T) and dims (PV)
   const int G = lane >> 4, li = lane & 15;
   const int h0 = blockIdx.y * (16 * HS) + 16 * hs;  // first head of this wave's set

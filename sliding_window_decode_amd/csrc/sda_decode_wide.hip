@@ -76,15 +76,6 @@ struct WideSmem {
   uint32_t vany[kNB];  // whether the tile has a valid row
 };
 
-// f(integral_constant<int, I>) for I = B .. E-1, each I a compile-time constant
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // DPP lane exchanges within groups of eight consecutive lanes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

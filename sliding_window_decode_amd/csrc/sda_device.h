@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -157,6 +159,15 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void dma16(uint64_t src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((gbl_void*)(uintptr_t)src, (lds_void*)lds_wave_base, 16, 0, 0);
 }
+// f(integral_constant<int, I>) for I = B .. E-1, each I a compile-time constant
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // The same with a constant byte offset OFF in the load's immediate. The hardware adds it to both addresses:
 // lane l's 16 bytes come from src + OFF and land at lds_wave_base + OFF + 16 l (probed on gfx950).
 template <int OFF>
