@@ -334,12 +334,13 @@ def plan_dict(plan):
             "whole_tokens": bool(plan.whole_tokens)}
 
 
-def measure(w, dw, plan, steps, warmup, cold=True):
+def measure(w, dw, plan, steps, warmup, cold=True, ramp=0.05):
     """Hot and (optionally) cold timings of one workload under one plan, with rooflines of the whole step
     and of the decode kernel."""
     byts, flops, rows = algorithmic_work(w)
     r = Runner(w, dw, plan)
-    r.ramp(0.05)
+    if ramp > 0:
+        r.ramp(ramp)
     st_h, k_h, ho_h = r.time(steps, warmup)
     res = {"plan": plan_dict(plan), "alg_bytes": byts, "alg_flops": flops, "valid_rows": rows,
            "hot": {"step_us": round(st_h * 1e3, 2), "kernel_us": round(k_h * 1e3, 2),
@@ -376,6 +377,8 @@ def main():
                     help="auto: the library's choice (sda_choose_plan); split: scheduler + combine; whole: one "
                          "workgroup per token")
     ap.add_argument("--hot", action="store_true", help="headline on hot buffers (the same buffers every call)")
+    ap.add_argument("--ramp", type=float, default=RAMP_S,
+                    help="seconds of untimed steps before the headline's warmup (0 under a profiler)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (calibrates the counter-based traffic)")
@@ -423,8 +426,8 @@ def main():
     if not args.hot:
         nsets, per_set = r.make_cold_sets()
         log(f"[bench] cold: {nsets} buffer sets of {per_set / 1e6:.1f} MB")
-    ramp_steps = r.ramp(RAMP_S)
-    log(f"[bench] clock ramp: {ramp_steps} untimed steps in {RAMP_S:.1f} s")
+    ramp_steps = r.ramp(args.ramp) if args.ramp > 0 else 0
+    log(f"[bench] clock ramp: {ramp_steps} untimed steps in {args.ramp:.2f} s")
     ms_step, ms_kern, ms_host = r.time(args.steps, max(args.warmup, len(r.sets)))
     log(f"[bench] step {ms_step * 1e3:.2f} us, decode kernel {ms_kern * 1e3:.2f} us, host enqueue "
         f"{ms_host * 1e3:.2f} us per step")
@@ -475,13 +478,13 @@ def main():
         pc = plan_for(wc)
         if args.precision is not None:
             pc.precision = args.precision
-        res, _ = measure(wc, dwc, pc, args.steps, args.warmup)
+        res, _ = measure(wc, dwc, pc, args.steps, args.warmup, ramp=min(args.ramp, 0.05))
         entry = {"heads": wc.H, "tokens": wc.T, **res}
         if name == HEADLINE and pc.whole_tokens:
             # the plan the configuration names: split-KV sized to 256 CUs + combine
             sp = sda.make_plan(wc.T, wc.H, wc.d_qk, wc.lst.width, wc.xlst.width if wc.xlst is not None else 0)
             sp.precision = pc.precision
-            entry["split_plan"], _ = measure(wc, dwc, sp, args.steps, args.warmup)
+            entry["split_plan"], _ = measure(wc, dwc, sp, args.steps, args.warmup, ramp=min(args.ramp, 0.05))
         per[name] = entry
         log(f"[bench]   {name}: hot {res['hot']['step_us']} us, cold {res['cold']['step_us']} us")
         if dwc is not dw:
