@@ -36,9 +36,10 @@ namespace sda {
 constexpr int KT = 32;    // rows per sub-tile
 constexpr int NSLOT = 3;  // address slots: sub-tiles k+1, k+2, k+3
 
-template <int DQK, int NH2>
+// Every format this kernel takes holds 512 dims (d_qk = d_v = 512).
+template <int NH2>
 struct DecodeSmem {
-  static constexpr int RS = DQK * 2;  // bytes per bf16 row
+  static constexpr int RS = 1024;  // bytes per bf16 row
   char tile[KT * RS];
   f32x4 spart[4][2][NH2][64];  // QK partials [wave][row block][head block][lane]
   float scale[KT][4];          // the four 128-dim scales of each row of the tile (0 = masked row)
@@ -51,12 +52,11 @@ struct DecodeSmem {
 
 // QR: built for V4.1 calls, whose query dims 448..511 come from the rotated buffer (a separate build, so
 // that the extra loads do not add to the register pressure of every other call)
-template <int DQK, int NH2, int NTERM, bool QR>
+template <int NH2, int NTERM, bool QR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NH2 == 1 ? 3 : 1)))
 void decode_kernel(DecodeParams p) {
-  constexpr int RS = DecodeSmem<DQK, NH2>::RS;
-  constexpr bool kRope = DQK == 576;
-  __shared__ DecodeSmem<DQK, NH2> sm;
+  constexpr int RS = DecodeSmem<NH2>::RS;
+  __shared__ DecodeSmem<NH2> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -73,12 +73,11 @@ void decode_kernel(DecodeParams p) {
 
   // ---- per-lane LDS bases (rows of a sub-tile start at multiples of 8, so a lane's swizzle term is
   // the same for every row it touches; every access below is base + a compile-time offset)
-  uint32_t kb[2], kr, vb[4];  // byte offsets into sm.tile
+  uint32_t kb[2], vb[4];  // byte offsets into sm.tile
   {
     const int f = ((li & 3) << 1) | ((li >> 2) & 1);  // K operand rows li (+16 rb)
     kb[0] = li * RS + 256 * w + 16 * (G ^ f);
     kb[1] = li * RS + 256 * w + 16 * ((4 + G) ^ f);
-    kr = li * RS + 16 * (64 + ((4 * (w & 1) + G) ^ f));
     const int rv = 4 * G + (li >> 2);  // V operand rows rv .. rv + 3 (+16)
     const int fv = ((rv & 3) << 1) | ((rv >> 2) & 1);
     const int cb = (li & 3) >> 1;
@@ -89,6 +88,7 @@ void decode_kernel(DecodeParams p) {
   // ---- slot ids -> addresses (threads 0..31, one row each)
   int pf_sid = -1;
   auto idx_issue = [&](const Item& it) {
+    const int tid = threadIdx.x + opaque_lane_zero();
     pf_sid = -1;
     if (!it.end() && tid < KT) {
       const int pos = it.pos0 + tid;
@@ -97,6 +97,7 @@ void decode_kernel(DecodeParams p) {
   };
   auto idx_finish = [&](const Item& it, int s) {
     if (w == 0) {
+      const int tid = threadIdx.x + opaque_lane_zero();
       const ListDev& ld = LD(it.L);
       const bool ok = !it.end() && tid < KT && pf_sid >= 0 && pf_sid < ld.slots;
       uint64_t a = 0, sa = 0;
@@ -116,57 +117,54 @@ void decode_kernel(DecodeParams p) {
   };
 
   // ---- record staging (registers): the sub-tile's data chunks, its scale chunk and bf16 chunk
-  // (MODEL1_584 rows: 28 code chunks, then 8 bf16 chunks for dims 448..511, loaded like the rope dims of
-  // d_qk 576 rows; the code loads of lanes 28..31 fall inside the record and are not used)
+  // (MODEL1_584 rows: 28 code chunks, then 8 bf16 chunks for dims 448..511, one per lane of 64; the code
+  // loads of lanes 28..31 fall inside the record and are not used).
+  // The issue is one branch-free sequence of loads, the same for every format: a load a format does not
+  // need reads the list's first record. A load under a format branch would leave its register merged
+  // with the value of the previous sub-tile where the branches join, and the compiler's copy there
+  // waits for the load, which would stall every sub-tile on a full memory round trip.
   u32x4 stg[4];
-  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; ue8m0 formats: the word holding its byte
-  u32x4 stg_sc;
+  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; ue8m0 formats: the 16-bit word holding its byte
+  uint32_t stg_s1;     // FP8_SLOTSCALE: the row's scale (lanes 0..31)
+  u32x4 stg_sc;        // FP8_528 / V32_656: the row's four fp32 scales (lanes 0..31)
   u32x4 stg_rp;
   auto rec_issue = [&](const Item& it, int s) {
-    if (it.end() || !sm.slot_any[s]) return;
+    const int tid = threadIdx.x + opaque_lane_zero();
     const ListDev& ld = LD(it.L);
     const uint64_t dummy = (uint64_t)ld.base;
-    if (ld.format == SDA_NVFP4_288) {
+    const int fmt = ld.format;
+    const bool fp4 = fmt == SDA_NVFP4_288;
+    const bool m1 = fmt == SDA_MODEL1_584;
+    // ends of the part and all-masked sub-tiles hold zero addresses (every load then reads the dummy)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int r = (tid >> 4) + 16 * k, c = tid & 15;
-        const uint64_t a = sm.addr[s][r];
-        stg[k] = ld_global_16(a ? a + 16 * c : dummy);
-        stg_sb[k] = ld_global_u16(a ? a + 256 + 2 * c : dummy);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = (tid >> 5) + 8 * k, c = tid & 31;
-        const uint64_t a = sm.addr[s][r];
-        stg[k] = ld_global_16(a ? a + 16 * c : dummy);
-        // FP8_UE8M0: chunk c (dims 16c .. 16c+15) takes scale byte c / 2: byte (c / 2) % 4 of word c / 8.
-        // MODEL1_584: scale byte c / 4 (64 dims each) of the 7 at byte 576: byte (c / 4) % 4 of word c / 16
-        if (ld.format == SDA_FP8_UE8M0) stg_sb[k] = *(gbl_u32*)(a ? a + 512 + 4 * (c >> 3) : dummy);
-        if constexpr (!kRope) {
-          if (ld.format == SDA_MODEL1_584) stg_sb[k] = *(gbl_u32*)(a ? a + 576 + 4 * (c >> 4) : dummy);
-        }
-      }
-      if (tid < KT && ld.format != SDA_FP8_UE8M0 && ld.format != SDA_MODEL1_584) {
-        const uint64_t sa = sm.saddr[s][tid];
-        if (ld.format == SDA_FP8_SLOTSCALE)
-          stg_sc[0] = *(gbl_u32*)(sa ? sa : dummy);
-        else
-          stg_sc = ld_global_16(sa ? sa : dummy);
-      }
-      if constexpr (kRope) {
-        const uint64_t a = sm.addr[s][tid >> 3];
-        stg_rp = ld_global_16(a ? a + 528 + 16 * (tid & 7) : dummy);
-      } else if (ld.format == SDA_MODEL1_584) {
-        const uint64_t a = sm.addr[s][tid >> 3];
-        stg_rp = ld_global_16(a ? a + 448 + 16 * (tid & 7) : dummy);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int r = fp4 ? (tid >> 4) + 16 * k : (tid >> 5) + 8 * k;
+      const int c = fp4 ? tid & 15 : tid & 31;
+      const uint64_t a = sm.addr[s][r & (KT - 1)];
+      const bool data = a != 0 && (k < 2 || !fp4);
+      stg[k] = ld_global_16(data ? a + 16 * c : dummy);
+      // NVFP4: u16 at byte 256 + 2c. FP8_UE8M0: chunk c (dims 16c .. 16c+15) takes scale byte 512 + c / 2.
+      // MODEL1_584: scale byte 576 + c / 4 (64 dims each). Each is read as the aligned 16-bit word holding it.
+      const int sb = fp4 ? 256 + 2 * c : fmt == SDA_FP8_UE8M0 ? 512 + ((c >> 1) & ~1) : 576 + ((c >> 2) & ~1);
+      const bool sbv = data && (fp4 || fmt == SDA_FP8_UE8M0 || m1);
+      stg_sb[k] = ld_global_u16(sbv ? a + sb : dummy);
+    }
+    {
+      const uint64_t sa = sm.saddr[s][tid & (KT - 1)];
+      const bool lo = tid < KT && sa != 0;
+      stg_s1 = *(gbl_u32*)(lo && fmt == SDA_FP8_SLOTSCALE ? sa : dummy);
+      stg_sc = ld_global_16(lo && (fmt == SDA_FP8_528 || fmt == SDA_V32_656) ? sa : dummy);
+    }
+    {
+      const uint64_t a = sm.addr[s][tid >> 3];
+      stg_rp = ld_global_16(a != 0 && m1 ? a + 448 + 16 * (tid & 7) : dummy);
     }
   };
   auto rec_convert = [&](const Item& it, int s) {
     const bool live = !it.end() && sm.slot_any[s];
     if (tid == 0) sm.tile_any = live ? 1 : 0;
     if (!live) return;
+    const int tid = threadIdx.x + opaque_lane_zero();
     const ListDev& ld = LD(it.L);
     if (ld.format == SDA_NVFP4_288) {
 #pragma unroll
@@ -195,7 +193,7 @@ void decode_kernel(DecodeParams p) {
       }
     } else {
       const bool ue8m0 = ld.format == SDA_FP8_UE8M0;
-      const bool m1 = !kRope && ld.format == SDA_MODEL1_584;
+      const bool m1 = ld.format == SDA_MODEL1_584;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int r = (tid >> 5) + 8 * k, c = tid & 31;
@@ -203,8 +201,8 @@ void decode_kernel(DecodeParams p) {
         const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
         // ue8m0 records: the power-of-two scale is applied by the conversion (the row's scale table
         // then holds 1); other formats convert unscaled
-        const float cs = ue8m0 ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 1) & 3)))
-                         : m1  ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 2) & 3)))
+        const float cs = ue8m0 ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 1) & 1)))
+                         : m1  ? ue8m0_scale(stg_sb[k] >> (8 * ((c >> 2) & 1)))
                                : 1.0f;
         uint32_t y[8];
         e4m3x4_to_bf16_scaled(x[0], cs, y[0], y[1]);
@@ -228,7 +226,7 @@ void decode_kernel(DecodeParams p) {
         const bool ok = sm.addr[s][tid] != 0;
         f32x4 sc;
         if (ld.format == SDA_FP8_SLOTSCALE) {
-          const float v = __builtin_bit_cast(float, stg_sc[0]);
+          const float v = __builtin_bit_cast(float, stg_s1);
           sc = f32x4{v, v, v, v};
         } else if (ue8m0 || m1) {
           sc = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -237,12 +235,7 @@ void decode_kernel(DecodeParams p) {
         }
         *(f32x4*)sm.scale[tid] = ok ? sc : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      if constexpr (kRope) {
-        const int r = tid >> 3, c = 64 + (tid & 7);
-        const bool ok = sm.addr[s][r] != 0;
-        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-        *(u32x4*)(sm.tile + r * RS + 16 * ((c & ~7) | ((c ^ f) & 7))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};
-      } else if (m1) {
+      if (m1) {
         const int r = tid >> 3, c = 56 + (tid & 7);
         const bool ok = sm.addr[s][r] != 0;
         const int f = ((r & 3) << 1) | ((r >> 2) & 1);
@@ -273,7 +266,6 @@ void decode_kernel(DecodeParams p) {
   __syncthreads();
 
   bf16x8 qreg[NH2][4];
-  bf16x8 qrope[NH2];
   f32x4 O[NH2][8];
   float m[NH2], l[NH2];
   bool token_start = true;
@@ -287,7 +279,7 @@ void decode_kernel(DecodeParams p) {
         const uint16_t* qh = qp + (int64_t)(h0 + 16 * hb + li) * p.q_sh;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = *(const bf16x8*)(qh + 32 * ks);
-        if constexpr (QR && !kRope) {
+        if constexpr (QR) {
           // V4.1 calls: dims 448..511 (wave 3, k-steps 2 and 3) from the rotated buffer [T][H][64]; the
           // lane's offset is recomputed here, behind an opaque zero, rather than kept live in the loop
           if (w == 3) {
@@ -297,7 +289,6 @@ void decode_kernel(DecodeParams p) {
             qreg[hb][3] = *(const bf16x8*)(qr + 32);
           }
         }
-        if constexpr (kRope) qrope[hb] = *(const bf16x8*)(qh - 128 * w + 512 + 32 * (w & 1));
 #pragma unroll
         for (int db = 0; db < 8; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[hb] = kNegInf;
@@ -326,14 +317,6 @@ void decode_kernel(DecodeParams p) {
           const float s = sm.scale[rb * 16 + 4 * G + r][w];
 #pragma unroll
           for (int hb = 0; hb < NH2; ++hb) acc[hb][r] *= s;
-        }
-        if constexpr (kRope) {
-          if (w < 2) {
-            const bf16x8 a = *(const bf16x8*)(sm.tile + kr + rb * 16 * RS);
-#pragma unroll
-            for (int hb = 0; hb < NH2; ++hb)
-              acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrope[hb], acc[hb], 0, 0, 0);
-          }
         }
 #pragma unroll
         for (int hb = 0; hb < NH2; ++hb) sm.spart[w][rb][hb][lane] = acc[hb];
@@ -410,6 +393,8 @@ void decode_kernel(DecodeParams p) {
 
     // ---- epilogue after the token's last sub-tile in this part
     if (it1.end() || it1.t != it0.t) {
+      const int lane_e = lane + opaque_lane_zero();
+      const int li = lane_e & 15, G = lane_e >> 4;
       const int t = it0.t;
       const int s_first = it0.s_first;
       const bool whole = it0.whole && !p.all_partial;
@@ -460,33 +445,31 @@ void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int DQK, int NH2, bool QR>
+template <int NH2, bool QR>
 static hipError_t launch_decode_q(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
   dim3 grid(num_parts, p.H / (16 * NH2));
   if (precision == 1)
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 1, QR>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NH2, 1, QR>), grid, dim3(256), 0, stream, p);
   else if (precision == 2)
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 2, QR>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NH2, 2, QR>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<DQK, NH2, 3, QR>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NH2, 3, QR>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int DQK, int NH2>
+template <int NH2>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, int precision, hipStream_t stream) {
-  if constexpr (DQK == 512) {
-    if (p.q_rope) return launch_decode_q<DQK, NH2, true>(p, num_parts, precision, stream);
-  }
-  return launch_decode_q<DQK, NH2, false>(p, num_parts, precision, stream);
+  if (p.q_rope) return launch_decode_q<NH2, true>(p, num_parts, precision, stream);
+  return launch_decode_q<NH2, false>(p, num_parts, precision, stream);
 }
 
+// The formats that route here (NVFP4_288, FP8_UE8M0, MODEL1_584, with FP8_SLOTSCALE or FP8_528 beside
+// them) all hold 512 dims.
 hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                                 hipStream_t stream) {
-  if (d_qk == 576)
-    return heads_per_group == 16 ? launch_decode_t<576, 1>(p, num_parts, precision, stream)
-                                 : launch_decode_t<576, 2>(p, num_parts, precision, stream);
-  return heads_per_group == 16 ? launch_decode_t<512, 1>(p, num_parts, precision, stream)
-                               : launch_decode_t<512, 2>(p, num_parts, precision, stream);
+  if (d_qk != 512) return hipErrorInvalidValue;
+  return heads_per_group == 16 ? launch_decode_t<1>(p, num_parts, precision, stream)
+                               : launch_decode_t<2>(p, num_parts, precision, stream);
 }
 
 }  // namespace sda
