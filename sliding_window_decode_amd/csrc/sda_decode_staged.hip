@@ -15,8 +15,9 @@
 //               LDS; sum of the four partials; online softmax in base 2 (the reference max moves only
 //               when a tile exceeds it by more than 8); O += P' V with P' = p x scale split into NTERM
 //               bf16 terms and V read transposed from the tile with ds_read_b64_tr_b16
-//   convert(k+1): the staged records -> exact bf16 codes in the row-major LDS tile (16-byte chunks
-//               XOR-swizzled), fp32 scales -> a 32 x 4 LDS table; then the records of k+2 are issued.
+//   convert(k+1): the staged records -> exact bf16 codes in the row-major LDS tile (rows padded and
+//               chunks swizzled against bank conflicts), fp32 scales -> a 32 x 4 LDS table; then the
+//               records of k+2 are issued.
 // After a token's last sub-tile in the part: the final bf16 output and LSE (sink folded in) when the
 // part holds the whole token, otherwise a normalized fp32 partial and its LSE for the combine kernel.
 // Sources: masked softmax attention (native_swa_decode.py, _fallback_batched_sdp); gather, validity
@@ -36,10 +37,20 @@ namespace sda {
 constexpr int KT = 32;    // rows per sub-tile
 constexpr int NSLOT = 3;  // address slots: sub-tiles k+1, k+2, k+3
 
+// bf16 tile rows: 1024 bytes of dims and 32 of padding. The LDS serves a 16-byte access of 16 lanes (256
+// bytes) per cycle, lanes that fall in the same 4-byte bank at different addresses taking turns; a row
+// stride of 1056 bytes puts row r's chunk c at 16-byte slot 2r + c modulo 16, and chunk c of rows with
+// bit 3 set is stored at chunk c ^ 1 (tile_swz). Then the QK^T operand reads (one chunk of 16 rows), the
+// transposed V reads (8 rows x 2 chunks x 8 bytes per 32 lanes) and the conversion's stores (16 chunks of
+// one row, see there) each hit distinct banks, and every offset that varies with the k-step or the dims
+// block stays an immediate.
+constexpr int kTileRS = 1056;
+__device__ __forceinline__ int tile_swz(int r) { return (r >> 3) & 1; }
+
 // Every format this kernel takes holds 512 dims (d_qk = d_v = 512).
 template <int NH2>
 struct DecodeSmem {
-  static constexpr int RS = 1024;  // bytes per bf16 row
+  static constexpr int RS = kTileRS;  // bytes per bf16 row (1024 of dims, then padding)
   char tile[KT * RS];
   f32x4 spart[4][2][NH2][64];  // QK partials [wave][row block][head block][lane]
   float scale[KT][4];          // the four 128-dim scales of each row of the tile (0 = masked row)
@@ -71,18 +82,17 @@ void decode_kernel(DecodeParams p) {
   const int bt = mt[0], bi = mt[1], et = mt[2], ei = mt[3], bk = mt[4];
   if (bt >= p.T || bt > et || (bt == et && bi >= ei)) return;
 
-  // ---- per-lane LDS bases (rows of a sub-tile start at multiples of 8, so a lane's swizzle term is
-  // the same for every row it touches; every access below is base + a compile-time offset)
-  uint32_t kb[2], vb[4];  // byte offsets into sm.tile
+  // ---- per-lane LDS bases (rows 16 apart have the same swizzle, so every access below is base + a
+  // compile-time offset).
+  // K operand (k-step ks): row li (+16 rb), chunk 16 w + 4 ks + G at kb + 64 ks. V operand (dims block db):
+  // row rv (+16), chunk 16 w + 2 db + cb, bytes 8 (li & 1) .. at vb + 32 db. (The swizzle flips only a
+  // chunk's bit 0, which G and cb hold.)
+  uint32_t kb, vb;  // byte offsets into sm.tile
   {
-    const int f = ((li & 3) << 1) | ((li >> 2) & 1);  // K operand rows li (+16 rb)
-    kb[0] = li * RS + 256 * w + 16 * (G ^ f);
-    kb[1] = li * RS + 256 * w + 16 * ((4 + G) ^ f);
-    const int rv = 4 * G + (li >> 2);  // V operand rows rv .. rv + 3 (+16)
-    const int fv = ((rv & 3) << 1) | ((rv >> 2) & 1);
+    kb = li * RS + 256 * w + 16 * (G ^ tile_swz(li));
+    const int rv = 4 * G + (li >> 2);
     const int cb = (li & 3) >> 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) vb[q] = rv * RS + 256 * w + 16 * ((2 * q + cb) ^ fv) + 8 * (li & 1);
+    vb = rv * RS + 256 * w + 16 * (cb ^ tile_swz(rv)) + 8 * (li & 1);
   }
 
   // ---- slot ids -> addresses (threads 0..31, one row each)
@@ -173,18 +183,21 @@ void decode_kernel(DecodeParams p) {
         const bool ok = sm.addr[s][r] != 0;
         const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
         const float s0 = e4m3_to_f32(stg_sb[k] & 0xFFu), s1 = e4m3_to_f32((stg_sb[k] >> 8) & 0xFFu);
-        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        const int f = tile_swz(r);
         char* row = sm.tile + r * RS;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sc = q < 2 ? s0 : s1;
+        for (int j = 0; j < 4; ++j) {
+          // the 16 lanes of row r store output chunks 4c + q together; q rotates with c so that the 16
+          // chunks are distinct modulo 16
+          const int q = (j + (c >> 1) + (c >> 3)) & 3;
+          const uint32_t xq = (q & 2) ? ((q & 1) ? x[3] : x[2]) : ((q & 1) ? x[1] : x[0]);
+          const float sc = (q & 2) ? s1 : s0;
           u32x4 o;
-          o[0] = e2m1x2_scaled_to_bf16<0>(x[q], sc);
-          o[1] = e2m1x2_scaled_to_bf16<1>(x[q], sc);
-          o[2] = e2m1x2_scaled_to_bf16<2>(x[q], sc);
-          o[3] = e2m1x2_scaled_to_bf16<3>(x[q], sc);
-          const int cc = 4 * c + q;
-          *(u32x4*)(row + 16 * ((cc & ~7) | ((cc ^ f) & 7))) = o;
+          o[0] = e2m1x2_scaled_to_bf16<0>(xq, sc);
+          o[1] = e2m1x2_scaled_to_bf16<1>(xq, sc);
+          o[2] = e2m1x2_scaled_to_bf16<2>(xq, sc);
+          o[3] = e2m1x2_scaled_to_bf16<3>(xq, sc);
+          *(u32x4*)(row + 16 * ((4 * c + q) ^ f)) = o;
         }
       }
       if (tid < KT) {
@@ -214,12 +227,15 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) y[i] = nan_scale ? 0x7FC07FC0u : y[i];
         }
-        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+        const int f = tile_swz(r);
         char* row = sm.tile + r * RS;
-        const int c0 = 2 * c, c1 = 2 * c + 1;
+        // output chunks 2c and 2c + 1; lanes with c & 8 store the odd one first, so that the 16 chunks of
+        // each store are distinct modulo 16
+        const bool odd_first = (c & 8) != 0;
+        const u32x4 ylo = u32x4{y[0], y[1], y[2], y[3]}, yhi = u32x4{y[4], y[5], y[6], y[7]};
         if (!m1 || c < 28) {  // MODEL1_584: bf16 chunks 56..63 come from the bf16 part below
-          *(u32x4*)(row + 16 * ((c0 & ~7) | ((c0 ^ f) & 7))) = u32x4{y[0], y[1], y[2], y[3]};
-          *(u32x4*)(row + 16 * ((c1 & ~7) | ((c1 ^ f) & 7))) = u32x4{y[4], y[5], y[6], y[7]};
+          *(u32x4*)(row + 16 * ((2 * c + (odd_first ? 1 : 0)) ^ f)) = odd_first ? yhi : ylo;
+          *(u32x4*)(row + 16 * ((2 * c + (odd_first ? 0 : 1)) ^ f)) = odd_first ? ylo : yhi;
         }
       }
       if (tid < KT) {
@@ -238,8 +254,7 @@ void decode_kernel(DecodeParams p) {
       if (m1) {
         const int r = tid >> 3, c = 56 + (tid & 7);
         const bool ok = sm.addr[s][r] != 0;
-        const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-        *(u32x4*)(sm.tile + r * RS + 16 * ((c & ~7) | ((c ^ f) & 7))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)(sm.tile + r * RS + 16 * (c ^ tile_swz(r))) = ok ? stg_rp : u32x4{0u, 0u, 0u, 0u};
       }
     }
     if (tid < KT) sm.valid[tid] = sm.addr[s][tid] != 0 ? 1 : 0;
@@ -307,7 +322,7 @@ void decode_kernel(DecodeParams p) {
         for (int hb = 0; hb < NH2; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(sm.tile + kb[ks & 1] + rb * 16 * RS + 128 * (ks >> 1));
+          const bf16x8 a = *(const bf16x8*)(sm.tile + kb + rb * 16 * RS + 64 * ks);
 #pragma unroll
           for (int hb = 0; hb < NH2; ++hb)
             acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[hb][ks], acc[hb], 0, 0, 0);
@@ -378,7 +393,7 @@ void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const char* v = sm.tile + vb[db & 3] + 128 * (db >> 2);
+        const char* v = sm.tile + vb + 32 * db;
         const bf16x4 v0 = lds_read_tr16(v);
         const bf16x4 v1 = lds_read_tr16(v + 16 * RS);
         const bf16x8 B = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
