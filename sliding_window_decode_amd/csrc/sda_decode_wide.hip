@@ -55,18 +55,39 @@ constexpr int kNB = 2;                              // ring buffers
 constexpr int kGW = 4;                              // gathering waves (0 .. 3)
 constexpr int kNI = (kNC + kGW - 1) / kGW;          // gather instructions per gathering wave and tile (11)
 constexpr int kPP = 20;                             // floats per (head, k-step) row of the weights array
+constexpr int kCS = 1088;                           // ring bytes per chunk of all 64 rows (1024 + 64)
 
+// The LDS serves a 16-byte access of 16 lanes, or an 8-byte access of 32, per cycle (256 bytes over 64
+// 4-byte banks); lanes in the same bank at different addresses take turns. The layouts below are padded
+// or swizzled so that every access of the kernel hits distinct banks.
+//
 // Ring buffers are chunk-major: chunk q (bytes 16 q .. 16 q + 15 of the record) of row r sits at byte
-// 1024 q + 16 r. One global -> LDS load then moves chunk q of all 64 rows (lane r: row r, lane-contiguous
-// destinations), its source the lane's record address plus a constant.
-__device__ __forceinline__ uint32_t ring_off(int q, int r) { return (uint32_t)(1024 * q + 16 * r); }
+// 1088 q + 16 r. One global -> LDS load then moves chunk q of all 64 rows (lane r: row r, lane-contiguous
+// destinations), its source the lane's record address plus a constant. (The 64 bytes after each chunk's
+// 1024 put the two chunks that a transposed V read takes at different banks.)
+__device__ __forceinline__ uint32_t ring_off(int q, int r) { return (uint32_t)(kCS * q + 16 * r); }
+
+// Partial scores are written lane-contiguously and read by the softmax lanes 32 rows apart: entry
+// (row block rb, 4-row group a, lane l) sits at lane slot l ^ 2 sx_swz(rb, a, l), so that the 16 lanes of
+// a softmax read, which take 8 (rb, a / 2, l / 32) combinations, hit 16 distinct slots.
+__device__ __forceinline__ int sx_slot(int rb, int a, int l) {
+  return l ^ ((((rb & 1) << 2) | (((a >> 1) & 1) << 1) | ((l >> 5) & 1)) << 1);
+}
+
+// softmax weights of one (head block, k-step): [head][8 hf + e] (16 of kPP used), then 16 floats that
+// offset the next k-step's block by 64 bytes modulo 256 (the softmax lanes store four k-steps at once)
+struct PwBlock {
+  float v[32][kPP];
+  float pad[16];
+};
 
 struct WideSmem {
-  char ring[kNB][kNC * 1024];
-  // partial scores: [dims half][head block][row block][4-row group a][lane] in the 32x32 accumulator layout
+  char ring[kNB][kNC * kCS];
+  // partial scores: [dims half][head block][row block][4-row group a][lane slot] in the 32x32 accumulator
+  // layout (sx_slot)
   f32x4 sx[2][2][2][4][64];
-  // softmax weights in the PV operand layout: [head block][k-step][head][8 hf + e] (16 of kPP used)
-  __attribute__((aligned(16))) float pw[2][4][32][kPP];
+  // softmax weights in the PV operand layout: [head block][k-step]
+  __attribute__((aligned(16))) PwBlock pw[2][4];
   // each row's four fp32 scales: [buffer][scale group][row]
   __attribute__((aligned(16))) float stab[kNB][4][kTileRows];
   // each row's additive score mask: 0 for a valid row, -inf for a masked one
@@ -190,12 +211,12 @@ void decode_wide_kernel(DecodeParams p) {
   };
   auto gather_issue = [&](uint64_t ra, int b) {
     const uint64_t src = ra + 16 * w;
-    char* dst = sm.ring[b] + 1024 * w;
+    char* dst = sm.ring[b] + kCS * w;
     static_assert(64 * (kNI - 1) < 4096, "offsets fit the load's immediate");
     static_for<0, kNI>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       // the immediate offset moves the LDS destination too: the base given is 64 i below chunk w + 4 i
-      if (w + kGW * i < kNC) dma16_at<64 * i>(src, dst + (1024 * kGW - 64) * i);
+      if (w + kGW * i < kNC) dma16_at<64 * i>(src, dst + (kCS * kGW - 64) * i);
     });
     dma4(ra + 512 + 4 * w, &sm.stab[b][w][0]);
   };
@@ -310,7 +331,7 @@ void decode_wide_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        sm.sx[qdh][qhb][qrb][a][lane] = f32x4{S[4 * a], S[4 * a + 1], S[4 * a + 2], S[4 * a + 3]};
+        sm.sx[qdh][qhb][qrb][a][sx_slot(qrb, a, lane)] = f32x4{S[4 * a], S[4 * a + 1], S[4 * a + 2], S[4 * a + 3]};
     }
     barrier_lds();  // partial scores visible
 
@@ -324,8 +345,8 @@ void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
       for (int a0 = 0; a0 < 2; ++a0) {
         const int a = 2 * sah + a0;
-        const f32x4 x0 = sm.sx[0][w >> 2][srb][a][src_lane];
-        const f32x4 x1 = sm.sx[1][w >> 2][srb][a][src_lane];
+        const f32x4 x0 = sm.sx[0][w >> 2][srb][a][sx_slot(srb, a, src_lane)];
+        const f32x4 x1 = sm.sx[1][w >> 2][srb][a][sx_slot(srb, a, src_lane)];
         const f32x4 mk = *(const f32x4*)&sm.mtab[b][32 * srb + 8 * a + 4 * shf];
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[a0][e] = __builtin_fmaf(x0[e] + x1[e], p.scale_log2, mk[e]);
@@ -348,7 +369,7 @@ void decode_wide_kernel(DecodeParams p) {
         }
       }
       // PV operand layout: k-step 2 srb + sah, row half shf, elements 4 a0 + e
-      float* pdst = &sm.pw[w >> 2][2 * srb + sah][8 * (w & 3) + h8][8 * shf];
+      float* pdst = &sm.pw[w >> 2][2 * srb + sah].v[8 * (w & 3) + h8][8 * shf];
       *(f32x4*)pdst = pv[0];
       *(f32x4*)(pdst + 4) = pv[1];
       l = l * alpha + ps;
@@ -411,8 +432,8 @@ void decode_wide_kernel(DecodeParams p) {
         {
           const f32x4 s0 = *(const f32x4*)&sm.stab[b][pg][16 * kk + 4 * hf];
           const f32x4 s1 = *(const f32x4*)&sm.stab[b][pg][16 * kk + 8 + 4 * hf];
-          const f32x4 p0 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf];
-          const f32x4 p1 = *(const f32x4*)&sm.pw[phb][kk][n][8 * hf + 4];
+          const f32x4 p0 = *(const f32x4*)&sm.pw[phb][kk].v[n][8 * hf];
+          const f32x4 p1 = *(const f32x4*)&sm.pw[phb][kk].v[n][8 * hf + 4];
           float pg8[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
