@@ -42,27 +42,44 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedParams p) {
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x;
   const int NT = blockDim.x;
-  int local = 0;
-  for (int t = tid; t < p.T; t += NT) {
+  // the first chunk's token (every token when T <= NT, the launch's usual shape): lengths read once,
+  // and its cost scan gives the total too
+  int n0c = 0, n1c = 0, costc = 0;
+  if (tid < p.T) {
+    n0c = clamp_len(p.lens[0], p.lens_div[0], p.width[0], tid);
+    n1c = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], tid) : 0;
+    costc = token_tiles(n0c, n1c) + p.F;
+  }
+  int local = costc;
+  for (int t = tid + NT; t < p.T; t += NT) {
     const int n0 = clamp_len(p.lens[0], p.lens_div[0], p.width[0], t);
     const int n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], t) : 0;
     local += token_tiles(n0, n1) + p.F;
   }
   int total = 0;
-  (void)block_incl_scan(local, wave_tot, total);
+  const int incl0 = block_incl_scan(local, wave_tot, total);
   const int Q = (int)part_quantum(total, p.num_parts);
+  const bool one_chunk = p.T <= NT;
   int carry = 0, split_carry = 0;
   for (int base = 0; base < p.T; base += NT) {
     const int t = base + tid;
-    int nt = 0, cost = 0, n0 = 0, n1 = 0;
-    if (t < p.T) {
-      n0 = clamp_len(p.lens[0], p.lens_div[0], p.width[0], t);
-      n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], t) : 0;
-      nt = token_tiles(n0, n1);
-      cost = nt + p.F;
+    int nt = 0, cost = 0, n0 = 0, n1 = 0, cum = 0, chunk_cost = 0;
+    if (one_chunk) {  // base == 0: the scan above is this chunk's
+      n0 = n0c;
+      n1 = n1c;
+      cost = costc;
+      nt = t < p.T ? cost - p.F : 0;
+      cum = incl0 - cost;
+      chunk_cost = total;
+    } else {
+      if (t < p.T) {
+        n0 = clamp_len(p.lens[0], p.lens_div[0], p.width[0], t);
+        n1 = p.nlists > 1 ? clamp_len(p.lens[1], p.lens_div[1], p.width[1], t) : 0;
+        nt = token_tiles(n0, n1);
+        cost = nt + p.F;
+      }
+      cum = carry + block_incl_scan(cost, wave_tot, chunk_cost) - cost;  // cost-axis start of t
     }
-    int chunk_cost = 0;
-    const int cum = carry + block_incl_scan(cost, wave_tot, chunk_cost) - cost;  // cost-axis start of t
     int nsplit = 0, pos0 = 0, p0 = 0, p1 = 0;
     if (t < p.T) {
       pos0 = cum + p.F;  // position of the token's first tile
