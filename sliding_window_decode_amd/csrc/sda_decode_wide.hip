@@ -209,16 +209,20 @@ void decode_wide_kernel(DecodeParams p) {
     }
     return ra;
   };
-  auto gather_issue = [&](uint64_t ra, int b) {
+  auto gather_issue_part = [&](uint64_t ra, int b, auto i0c, auto i1c) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
     const uint64_t src = ra + 16 * w;
     char* dst = sm.ring[b] + kCS * w;
     static_assert(64 * (kNI - 1) < 4096, "offsets fit the load's immediate");
-    static_for<0, kNI>([&](auto ic) {
+    static_for<I0, I1>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       // the immediate offset moves the LDS destination too: the base given is 64 i below chunk w + 4 i
       if (w + kGW * i < kNC) dma16_at<64 * i>(src, dst + (kCS * kGW - 64) * i);
     });
-    dma4(ra + 512 + 4 * w, &sm.stab[b][w][0]);
+    if constexpr (I1 == kNI) dma4(ra + 512 + 4 * w, &sm.stab[b][w][0]);
+  };
+  auto gather_issue = [&](uint64_t ra, int b) {
+    gather_issue_part(ra, b, std::integral_constant<int, 0>{}, std::integral_constant<int, kNI>{});
   };
 
   // ---- prologue: items k = 0 .. 2, the gather of tile 0 in flight, the slot ids of tile 1
@@ -334,6 +338,8 @@ void decode_wide_kernel(DecodeParams p) {
         sm.sx[qdh][qhb][qrb][a][sx_slot(qrb, a, lane)] = f32x4{S[4 * a], S[4 * a + 1], S[4 * a + 2], S[4 * a + 3]};
     }
     barrier_lds();  // partial scores visible
+    // the first three of the gather loads of tile k+1 (the rest follow the softmax, below)
+    if (gath) gather_issue_part(ra_next, b ^ 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
 
     // Q of the next tile's token (the registers are free until its QK^T)
     if (!it1.end() && it1.t != it0.t) load_q(it1.t);
@@ -396,11 +402,13 @@ void decode_wide_kernel(DecodeParams p) {
       l = 0.f;
     }
     barrier_lds();  // weights, rescale factors and output factors visible
-    // The gather loads of tile k+1, issued here rather than with the addresses above: the address unit takes
-    // about as long to accept a tile's loads as a SIMD needs for one wave's PV, so waves 0 .. 3 wait for it
-    // while waves 4 .. 7, which share their SIMDs, run their PV products (issued at the top of the tile
-    // they held waves 0 .. 3 past the QK^T that waves 4 .. 7 finish sooner).
-    if (gath) gather_issue(ra_next, b ^ 1);
+    // The rest of the gather loads of tile k+1, issued here rather than with the addresses above: the address
+    // unit takes about as long to accept a tile's loads as a SIMD needs for one wave's PV, so waves 0 .. 3
+    // wait for it while waves 4 .. 7, which share their SIMDs, run their PV products (issued at the top of
+    // the tile they held waves 0 .. 3 past the QK^T that waves 4 .. 7 finish sooner; three of the eleven
+    // issued before the softmax let the tile land sooner at little cost to it: 1-2 % faster than none or
+    // six).
+    if (gath) gather_issue_part(ra_next, b ^ 1, std::integral_constant<int, 3>{}, std::integral_constant<int, kNI>{});
 
     // ---- PV over dims 128 pg .. 128 pg + 127 of heads 32 phb .. 32 phb + 31
     {
