@@ -213,11 +213,14 @@ void decode_wide_kernel(DecodeParams p) {
     constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
     const uint64_t src = ra + 16 * w;
     char* dst = sm.ring[b] + kCS * w;
-    static_assert(64 * (kNI - 1) < 4096, "offsets fit the load's immediate");
+    // load i moves chunk w + kGW i: source byte 16 (w + kGW i) of the record, the kGW i part carried in the
+    // load's immediate, which the hardware adds to the LDS destination too (the base given is that much
+    // below chunk w + kGW i); chunks past the record's last (w + kGW i >= kNC) are not loaded
+    static_assert(16 * kGW * (kNI - 1) < 4096, "offsets fit the load's immediate");
+    static_assert(kGW == 4, "the four gathering waves load one scale group each");
     static_for<I0, I1>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      // the immediate offset moves the LDS destination too: the base given is 64 i below chunk w + 4 i
-      if (w + kGW * i < kNC) dma16_at<64 * i>(src, dst + (kCS * kGW - 64) * i);
+      if (w + kGW * i < kNC) dma16_at<16 * kGW * i>(src, dst + (kCS - 16) * kGW * i);
     });
     if constexpr (I1 == kNI) dma4(ra + 512 + 4 * w, &sm.stab[b][w][0]);
   };

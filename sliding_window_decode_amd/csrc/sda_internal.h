@@ -128,7 +128,7 @@ hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_pe
                               hipStream_t stream);
 hipError_t launch_decode_staged(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
                                 hipStream_t stream);
-// 576-dim records at 64 heads per workgroup (sda_decode_wide.hip: four waves of 32x32 products, every
+// 576-dim records at 64 heads per workgroup (sda_decode_wide.hip: eight waves of 32x32 products, every
 // widened operand fragment feeding 32 heads).
 hipError_t launch_decode_wide(const DecodeParams& p, int num_parts, int precision, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int num_parts, int heads_per_group, int d_qk, int precision,
