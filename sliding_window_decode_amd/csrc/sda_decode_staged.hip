@@ -9,7 +9,7 @@
 // Pipeline per workgroup, sub-tile k:
 //   slot ids of sub-tile k+3 are loaded while sub-tile k computes (they become record addresses at
 //   the end of the iteration); the records of sub-tile k+1 are already in flight in registers (issued
-//   one iteration earlier, branch-free: masked rows read a dummy address and are zeroed later).
+//   one iteration earlier, branch-free: masked rows read zeros and their data is zeroed again later).
 //   compute(k): QK^T partial over the wave's 128 dims (one dequant scale group) with
 //               v_mfma_f32_16x16x32_bf16, KV rows on M, heads on N; partial x that group's scale ->
 //               LDS; sum of the four partials; online softmax in base 2 (the reference max moves only
@@ -33,6 +33,13 @@
 #include "sda_items.h"
 
 namespace sda {
+
+// The loads a row or a format does not need read these zeros: the data of a masked row is zeroed at
+// conversion anyway, but its block scale or exponent is used, and zero bytes give a finite one (the
+// cache's own first bytes could read as a NaN scale, and 0 x NaN would reach the tile).
+namespace {
+__device__ __attribute__((aligned(16))) uint8_t g_zero_staged[64];
+}  // namespace
 
 constexpr int KT = 32;    // rows per sub-tile
 constexpr int NSLOT = 3;  // address slots: sub-tiles k+1, k+2, k+3
@@ -137,7 +144,7 @@ void decode_kernel(DecodeParams p) {
   // (MODEL1_584 rows: 28 code chunks, then 8 bf16 chunks for dims 448..511, one per lane of 64; the code
   // loads of lanes 28..31 fall inside the record and are not used).
   // The issue is one branch-free sequence of loads, the same for every format of the build's set (LS):
-  // a load a format does not need reads the list's first record. A load under a format branch would leave
+  // a load a row or a format does not need reads g_zero_staged. A load under a format branch would leave
   // its register merged with the value of the previous sub-tile where the branches join, and the
   // compiler's copy there waits for the load, which would stall every sub-tile on a full memory round
   // trip. Registers of loads outside the set hold zero.
@@ -149,11 +156,11 @@ void decode_kernel(DecodeParams p) {
   auto rec_issue = [&](const Item& it, int s) {
     const int tid = threadIdx.x + opaque_lane_zero();
     const ListDev& ld = LD(it.L);
-    const uint64_t dummy = (uint64_t)ld.base;
+    const uint64_t dummy = (uint64_t)(const void*)g_zero_staged;
     const int fmt = ld.format;
     const bool fp4 = fmt == SDA_NVFP4_288;
     const bool m1 = fmt == SDA_MODEL1_584;
-    // ends of the part and all-masked sub-tiles hold zero addresses (every load then reads the dummy)
+    // ends of the part and all-masked sub-tiles hold zero addresses (every load then reads the zeros)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = fp4 ? (tid >> 4) + 16 * k : (tid >> 5) + 8 * k;

@@ -224,6 +224,24 @@ def test_lens_beyond_width_and_negative():
     _run_cmp(w, "lens clamp")
 
 
+@pytest.mark.parametrize("fmt,xfmt,H", [(wl.FP8_528, wl.NVFP4_288, 16), (wl.FP8_SLOTSCALE, wl.NVFP4_288, 16),
+                                        (wl.NVFP4_288, None, 32), (wl.FP8_UE8M0, wl.NVFP4_288, 16)])
+def test_masked_rows_whatever_the_first_record_holds(fmt, xfmt, H):
+    """Masked rows (slot -1, out of range, past the length) contribute nothing whatever bytes the cache's
+    first record holds: here 0x7F 0xFF, the e2m1 pairs (-6, 6) and (-6, -6), which read as e4m3 block scales
+    (or as a ue8m0 exponent) would be NaN. Slot 0 itself is left out of every list."""
+    w = wl.small_workload(62, fmt, xfmt, T=6, H=H, width=100, xwidth=150 if xfmt is not None else 0, sink=True)
+    for c, L in w.lists():
+        c.data[0:2] = [0x7F, 0xFF]
+        L.idx[L.idx == 0] = -1
+        L.idx[:, ::5] = -1
+    w.lst.lens[:] = [100, 37, 1, 99, 64, 0]
+    if w.xlst is not None:
+        w.xlst.lens[:] = [150, 65, 2, 149, 0, 127]
+    _, out, _ = _run_cmp(w, "first record bytes")
+    assert not torch.isnan(out.float()).any()
+
+
 def test_page_stride_padding_and_small_pages():
     w = wl.small_workload(58, wl.FP8_528, wl.NVFP4_288, T=4, H=16, width=128, xwidth=128, num_slots=1024,
                           page_size=16, pad_bytes=272, sink=True)
