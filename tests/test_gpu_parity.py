@@ -430,10 +430,12 @@ def test_every_e2m1_code_and_block_scale():
 
 # ------------------------------------------------------------------ scheduler and combine through the ABI
 
-@pytest.mark.parametrize("P,F", [(1, 2), (256, 2), (513, 0), (4096, 5)])
-def test_device_scheduler_matches_host(P, F):
-    rng = np.random.default_rng(P)
-    T = 700
+@pytest.mark.parametrize("T,P,F", [(700, 1, 2), (700, 256, 2), (700, 513, 0), (700, 4096, 5), (1024, 768, 0),
+                                   (1025, 768, 0), (1025, 97, 3), (3000, 256, 2), (3000, 5000, 1)])
+def test_device_scheduler_matches_host(T, P, F):
+    """The device scheduler against its host twin; T above 1024 takes the kernel's chunked pass (the
+    lengths read per chunk of 1024 tokens, the scans carried across chunks)."""
+    rng = np.random.default_rng(P + T)
     lens = rng.integers(-3, 140, size=T).astype(np.int32)
     xl = rng.integers(0, 2049, size=T).astype(np.int32)
     plan = sda.sda_plan(P, 16, F, 3)
@@ -446,6 +448,17 @@ def test_device_scheduler_matches_host(P, F):
     torch.cuda.synchronize()
     assert np.array_equal(meta.cpu().numpy(), meta_h)
     assert np.array_equal(ns.cpu().numpy(), ns_h)
+
+
+def test_split_call_with_more_tokens_than_a_scheduler_chunk():
+    """A split call of 1100 tokens (the scheduler's chunked pass) against the oracle, every token."""
+    w = wl.small_workload(71, wl.FP8_528, wl.FP8_528, T=1100, H=16, width=64, xwidth=96, num_slots=4096,
+                          sink=True)
+    plan = auto_plan_for(w)
+    plan.whole_tokens = 0
+    plan.num_parts = 768
+    plan.fixed_overhead = 1
+    _run_cmp(w, "T = 1100 split", plan=plan)
 
 
 def test_combine_splits_against_oracle_merge():
