@@ -722,10 +722,10 @@ hipError_t launch_decode_ring(const DecodeParams& p, int num_parts, int heads_pe
                               hipStream_t stream) {
   const int kind = p.lst[0].format == SDA_FP8_UE8M0 ? kRingUe8m0
                    : p.lst[0].format == SDA_MODEL1_584 ? kRingModel1 : kRingF32Scales;
-  if (d_qk == 576) {
+  if (d_qk == 576) {  // 64 heads of 576-dim records run the wide kernel
     if (heads_per_group == 16) return launch_ring_any<576, 1, 2>(p, num_parts, precision, kRingF32Scales, stream);
     if (heads_per_group == 32) return launch_ring_any<576, 2, 3>(p, num_parts, precision, kRingF32Scales, stream);
-    return launch_ring_any<576, 4, 3>(p, num_parts, precision, kRingF32Scales, stream);
+    return hipErrorInvalidValue;
   }
   if (heads_per_group == 16) {
     if (kind == kRingModel1) return hipErrorInvalidValue;
