@@ -182,14 +182,17 @@ size_t sda_workspace_bytes(int T, int H, int d_v, const sda_plan* plan /*host*/)
  * num_splits[begin_token]; parts with no tiles hold {T, 0, T, 0, 0, 0, 0, 0}) and
  * num_splits [T+1] int32, the exclusive prefix sum of the number of parts that touch each token.
  * The result depends only on the lengths, so one call can serve every layer of a decode step.
- * extra may be NULL. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG. */
+ * extra may be NULL. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG. Tile positions are
+ * counted in 32-bit integers: T x (ceil(width/64) + ceil(extra_width/64) + 1 + fixed_overhead) at or
+ * above 2^31 gives SDA_ERR_UNSUPPORTED. */
 int sda_get_sched_meta(int T, const sda_list* list /*host*/, const sda_list* extra /*host, nullable*/,
                        const sda_plan* plan /*host*/, int32_t* meta, int32_t* num_splits, void* stream);
 
 /* Host only. The same schedule as sda_get_sched_meta, computed on the calling thread from host
  * copies of the lengths (lens / extra_lens: one int32 per queries_per_len tokens, as in sda_list, or
  * NULL = width) into host arrays meta [num_parts][SDA_META_INTS] and num_splits [T+1]. For callers
- * that keep lengths on the host. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG. */
+ * that keep lengths on the host. A whole-token plan has no schedule: SDA_ERR_INVALID_ARG; the same
+ * 2^31 bound on tile positions as sda_get_sched_meta. */
 int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens /*host, nullable*/, int width,
                             const int32_t* extra_lens /*host, nullable*/, int extra_width /*0 = no extra list*/,
                             const sda_plan* plan /*host*/, int32_t* meta /*host*/, int32_t* num_splits /*host*/);
@@ -211,7 +214,8 @@ int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens /*ho
  *             strides multiples of 8 elements, 16-byte aligned.
  *  lse        fp32 [T][H] at lse[t*lse_stride_t + h]: ln(exp(sink_h) + sum_i exp(z_i)); a token with
  *             no valid row gets out = 0 and lse = sink_h (-inf without a sink).
- * H in {16, 32, 64, 128}; (d_qk, d_v) in {(512, 512), (576, 512)}; 1 <= T. */
+ * H in {16, 32, 64, 128}; (d_qk, d_v) in {(512, 512), (576, 512)}; 1 <= T; a split plan also needs
+ * the scheduler's 2^31 bound on tile positions (sda_get_sched_meta), else SDA_ERR_UNSUPPORTED. */
 int sda_sparse_decode_attn(const void* q, int64_t q_stride_t, int64_t q_stride_h, int T, int H, int d_qk, int d_v,
                            const sda_cache* cache /*host*/, const sda_list* list /*host*/,
                            const sda_cache* extra_cache /*host, nullable*/, const sda_list* extra_list /*host, nullable*/,

@@ -104,6 +104,15 @@ int check_plan(const sda_plan* plan, int H) {
   return SDA_OK;
 }
 
+// The schedulers (device and host) and the decode kernels' part walk count tile positions in 32-bit
+// integers: T x (the most tiles a token can take + fixed_overhead) must stay below 2^31.
+int check_cost_range(int T, int width, int extra_width, const sda_plan* plan) {
+  const int64_t per_token = ((int64_t)width + 63) / 64 + ((int64_t)extra_width + 63) / 64 + 1 + plan->fixed_overhead;
+  if ((int64_t)T * per_token >= (int64_t(1) << 31))
+    return fail(SDA_ERR_UNSUPPORTED, "T x (tiles per token + fixed_overhead) must stay below 2^31");
+  return SDA_OK;
+}
+
 struct WorkspaceLayout {
   size_t o_acc, lse_acc, meta, num_splits, total;
   size_t q_rot, total_v41;  // V4.1 calls: the rotated q after everything else
@@ -353,6 +362,7 @@ int sda_get_sched_meta(int T, const sda_list* list, const sda_list* extra, const
   if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
   if (plan->whole_tokens) return fail(SDA_ERR_INVALID_ARG, "a whole-token plan has no schedule");
   if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
+  if ((rc = check_cost_range(T, list->width, extra ? extra->width : 0, plan))) return rc;
   hipError_t e = sda::launch_sched(sched_params(T, list, extra, plan, meta, num_splits), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sched kernel launch");
   return SDA_OK;
@@ -366,6 +376,7 @@ int sda_get_sched_meta_host(int T, int queries_per_len, const int32_t* lens, int
   if (!plan || plan->num_parts < 1 || plan->fixed_overhead < 0) return fail(SDA_ERR_INVALID_ARG, "bad plan");
   if (plan->whole_tokens) return fail(SDA_ERR_INVALID_ARG, "a whole-token plan has no schedule");
   if (!meta || !num_splits) return fail(SDA_ERR_INVALID_ARG, "meta and num_splits are required");
+  if (int rc = check_cost_range(T, width, extra_width, plan)) return rc;
   const int P = plan->num_parts, F = plan->fixed_overhead;
   int64_t total = 0;
   for (int t = 0; t < T; ++t) {
@@ -444,6 +455,9 @@ int check_decode_args(const void* q, int64_t q_stride_t, int64_t q_stride_h, int
     if ((rc = check_list(extra_list, "extra"))) return rc;
   }
   if ((rc = check_plan(plan, H))) return rc;
+  if (!plan->whole_tokens &&
+      (rc = check_cost_range(T, list->width, extra_list ? extra_list->width : 0, plan)))
+    return rc;
   if ((meta == nullptr) != (num_splits == nullptr))
     return fail(SDA_ERR_INVALID_ARG, "meta and num_splits must be given together");
   if (plan->whole_tokens && meta)

@@ -123,6 +123,8 @@ def _call(q_shape=(4, 16, 512), fmt=sda.FP8_528, page_size=64, page_stride=None,
     (dict(ws_bytes=1024), sda.SDA_ERR_WORKSPACE),                          # workspace too small
     (dict(q_ptr=(1 << 20) + 2), sda.SDA_ERR_INVALID_ARG),                  # q misaligned
     (dict(meta=True), sda.SDA_ERR_INVALID_ARG),                            # meta without num_splits
+    (dict(q_shape=(1 << 21, 16, 512), plan=sda.sda_plan(8, 16, 1024, 3)),
+     sda.SDA_ERR_UNSUPPORTED),                                              # tile positions reach 2^31
 ])
 def test_decode_rejects_bad_arguments_on_the_host(kw, status):
     if kw.get("meta"):
@@ -142,6 +144,22 @@ def test_decode_rejects_bad_arguments_on_the_host(kw, status):
         _call(**kw)
     assert ei.value.status == status
     assert sda.lib().sda_last_error()
+
+
+def test_schedulers_reject_tile_positions_past_32_bits():
+    """Both schedulers count tile positions in 32-bit integers: a call whose T x (tiles per token + F) reaches
+    2^31 is refused before anything runs; one just below it is accepted by the host scheduler."""
+    plan = sda.sda_plan(8, 16, 1024, 3)
+    T = (1 << 31) // (2 + 1 + 1024) + 1   # width 128: two tiles a token, one empty-tile allowance, F = 1024
+    with pytest.raises(sda.SdaError) as ei:
+        sda.get_sched_meta_host(T, None, 128, None, 0, plan)
+    assert ei.value.status == sda.SDA_ERR_UNSUPPORTED
+    lst = sda.SlotList(_FakeTensor((T, 128), 1 << 27), 128, None)
+    with pytest.raises(sda.SdaError) as ei:
+        sda.get_sched_meta(T, lst, None, plan, _FakeTensor((8, 8), 1 << 28), _FakeTensor((T + 1,), 1 << 29), stream=0)
+    assert ei.value.status == sda.SDA_ERR_UNSUPPORTED
+    meta, ns = sda.get_sched_meta_host(T - 1, None, 128, None, 0, plan)
+    assert ns[-1] >= T - 1
 
 
 def test_extra_cache_without_list_is_rejected():
