@@ -68,11 +68,12 @@ struct DecodeSmem {
   int slot_any[NSLOT];
 };
 
-// The record loads a build issues besides the four data chunks and the scale words of chunks 0..1 of each
-// lane (NVFP4 block scales, FP8_UE8M0 / MODEL1_584 exponents): the slot's scale (FP8_SLOTSCALE), the four
-// fp32 scales (FP8_528), and for FP8_UE8M0 / MODEL1_584 the scale words of chunks 2..3 and MODEL1's bf16
-// chunks. A call builds the set from its lists' formats; a load the set leaves out is not issued at all
-// (C4, FP8_528 beside NVFP4: 7 loads a lane and sub-tile instead of 11, decode kernel 4 % faster).
+// The record loads a build issues besides the four data chunks of each lane: the slot's scale
+// (FP8_SLOTSCALE), the four fp32 scales (FP8_528), and for FP8_UE8M0 / MODEL1_584 the exponent word of
+// each chunk and MODEL1's bf16 chunks. A call builds the set from its lists' formats; a load the set leaves
+// out is not issued at all. Without FP8_UE8M0 / MODEL1_584 lists an NVFP4 lane, which needs two data
+// chunks, loads its rows' 16-byte blocks of e4m3 scales into the other two (C4, FP8_528 beside NVFP4: 5
+// loads a lane and sub-tile instead of 11).
 enum StagedLoads { kLdSlotScale = 1, kLdF32Scales = 2, kLdMx = 4, kLdAll = 7 };
 
 // QR: built for V4.1 calls, whose query dims 448..511 come from the rotated buffer (a separate build, so
@@ -149,7 +150,7 @@ void decode_kernel(DecodeParams p) {
   // compiler's copy there waits for the load, which would stall every sub-tile on a full memory round
   // trip. Registers of loads outside the set hold zero.
   u32x4 stg[4];
-  uint32_t stg_sb[4];  // NVFP4: the chunk's two e4m3 block scales; ue8m0 formats: the 16-bit word holding its byte
+  uint32_t stg_sb[4];  // builds with ue8m0 formats: NVFP4 chunks' two e4m3 block scales, or the 16-bit word holding a ue8m0 byte
   uint32_t stg_s1;     // FP8_SLOTSCALE: the row's scale (lanes 0..31)
   u32x4 stg_sc;        // FP8_528 / V32_656: the row's four fp32 scales (lanes 0..31)
   u32x4 stg_rp;
@@ -163,16 +164,20 @@ void decode_kernel(DecodeParams p) {
     // ends of the part and all-masked sub-tiles hold zero addresses (every load then reads the zeros)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int r = fp4 ? (tid >> 4) + 16 * k : (tid >> 5) + 8 * k;
+      // builds without ue8m0 or MODEL1 formats: an NVFP4 lane's chunks 2 and 3 take the 16-byte block of
+      // scales (bytes 256 + 16 (c / 8) ..) of its rows of chunks 0 and 1, in place of two 16-bit loads
+      constexpr bool kScInData = (LS & kLdMx) == 0;
+      const int r = fp4 ? (tid >> 4) + 16 * (kScInData ? (k & 1) : k) : (tid >> 5) + 8 * k;
       const int c = fp4 ? tid & 15 : tid & 31;
       const uint64_t a = sm.addr[s][r & (KT - 1)];
-      const bool data = a != 0 && (k < 2 || !fp4);
-      stg[k] = ld_global_16(data ? a + 16 * c : dummy);
+      const bool data = a != 0 && (k < 2 || !fp4 || kScInData);
+      const int off = (fp4 && k >= 2) ? 256 + 16 * (c >> 3) : 16 * c;
+      stg[k] = ld_global_16(data ? a + off : dummy);
       // NVFP4: u16 at byte 256 + 2c. FP8_UE8M0: chunk c (dims 16c .. 16c+15) takes scale byte 512 + c / 2.
       // MODEL1_584: scale byte 576 + c / 4 (64 dims each). Each is read as the aligned 16-bit word holding it.
       const int sb = fp4 ? 256 + 2 * c : fmt == SDA_FP8_UE8M0 ? 512 + ((c >> 1) & ~1) : 576 + ((c >> 2) & ~1);
       const bool sbv = data && (fp4 || fmt == SDA_FP8_UE8M0 || m1);
-      if (k < 2 || (LS & kLdMx))
+      if constexpr ((LS & kLdMx) != 0)
         stg_sb[k] = ld_global_u16(sbv ? a + sb : dummy);
       else
         stg_sb[k] = 0u;
@@ -208,7 +213,16 @@ void decode_kernel(DecodeParams p) {
         const int r = (tid >> 4) + 16 * k, c = tid & 15;
         const bool ok = sm.addr[s][r] != 0;
         const u32x4 x = ok ? stg[k] : u32x4{0u, 0u, 0u, 0u};
-        const float s0 = e4m3_to_f32(stg_sb[k] & 0xFFu), s1 = e4m3_to_f32((stg_sb[k] >> 8) & 0xFFu);
+        uint32_t sbw;
+        if constexpr ((LS & kLdMx) != 0) {
+          sbw = stg_sb[k];
+        } else {  // the chunk's two scale bytes: bytes 2 (c % 8) .. of the row's block of scales
+          const u32x4 sv = stg[2 + k];
+          const int wi = (c & 7) >> 1;
+          const uint32_t wv = (wi & 2) ? ((wi & 1) ? sv[3] : sv[2]) : ((wi & 1) ? sv[1] : sv[0]);
+          sbw = wv >> (16 * (c & 1));
+        }
+        const float s0 = e4m3_to_f32(sbw & 0xFFu), s1 = e4m3_to_f32((sbw >> 8) & 0xFFu);
         const int f = tile_swz(r);
         char* row = sm.tile + r * RS;
 #pragma unroll
